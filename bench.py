@@ -1,0 +1,223 @@
+"""Throughput of the greedy speculative-verification step on one MI355X.
+
+A step = one verifier pass (moe_verify_step over B*(K+1) positions through all MoE
+blocks and the LM head) + greedy acceptance (accept_greedy), on seeded synthetic
+inputs already resident in HBM. The metric counts verified tokens: the tokens a pass
+commits, sum_b (accepted_b + 1).
+
+Default workload: 12 MoE blocks + LM head at hidden 1280, 64 routed top-6 + 2 shared
+experts, intermediate 896, vocabulary 129,280, bf16 weights; B = 32 sequences, K = 3
+drafts (128 positions); drafts agree with the verifier with probability 0.576.
+
+Prints one JSON line. Run: python bench.py [--steps K] [--warmup W] [--workload NAME]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA peak
+
+METRIC = "verified tokens/sec per verify step (B=32,K=3,12 layers); % HBM roofline"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def algorithmic(wl, counts):
+    """Algorithmic HBM bytes and flops of one step, from the step's actual routing.
+
+    Bytes: per block, the weights of every routed expert that received a slot plus the
+    shared experts (3*H*I elements each) and the router (E*H); the LM head (V*H); the
+    hidden states in (T*H fp32) and the argmax out (T*4). Intermediate buffers are not
+    counted. Flops: 2 per multiply-add of the router, the experts' T*(k+S) rows and the
+    LM head.
+    """
+    w = 2 if wl.wdtype == "bf16" else 4
+    H, I, E, S, k, V, T = wl.hidden, wl.inter, wl.n_routed, wl.n_shared, wl.top_k, wl.vocab, wl.positions
+    touched = (counts > 0).sum(axis=1)  # per block
+    expert_bytes = [(int(n) + S) * 3 * H * I * w for n in touched]
+    total = sum(expert_bytes) + wl.n_layers * E * H * w + V * H * w + T * H * 4 + T * 4
+    up_bytes = [(int(n) + S) * 2 * H * I * w for n in touched]
+    flops = wl.n_layers * (T * (k + S) * 6 * H * I + 2 * T * E * H) + 2 * T * V * H
+    return {"step_bytes": total, "up_bytes_per_launch": float(np.mean(up_bytes)),
+            "down_bytes_per_launch": float(np.mean([(int(n) + S) * H * I * w for n in touched])),
+            "lm_bytes": V * H * w, "flops": flops, "touched_per_block": float(np.mean(touched))}
+
+
+def cpu_baseline(wl, weights, x, drafts_fn):
+    """The CPU oracle, as it stands, on one full verifier pass of the same workload."""
+    import oracle as O
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    ref = O.verify_step(wl, weights, x)
+    n, _ = O.accept(drafts_fn(ref["ids"]), ref["ids"], wl.batch, wl.drafts)
+    dt = time.perf_counter() - t0
+    committed = int(n.sum()) + wl.batch
+    return {"value": committed / dt, "unit": "verified tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"one full verifier pass of {wl.name} ({wl.positions} positions, {wl.n_layers} blocks + LM "
+                      f"head) and its acceptance, float64 numpy, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode_b32_k3")
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of a HIP graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the verify step is "
+              "data-parallel over sequences with no exchange, see the design notes.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from lossless_speculative_verification_amd import binding as bnd
+    from lossless_speculative_verification_amd import workload as W
+
+    wl = W.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[bench] {wl.name}: generating weights")
+    t0 = time.perf_counter()
+    weights = W.make_weights(wl)
+    x_h = W.make_hidden(wl)
+    log(f"[bench] generated in {time.perf_counter() - t0:.1f} s; uploading + repacking")
+    dw = bnd.upload_weights(weights, dev)
+    ctx = bnd.MoeVerify(wl, dw)
+    del dw
+    torch.cuda.empty_cache()
+
+    T, B, K = wl.positions, wl.batch, wl.drafts
+    x = torch.from_numpy(x_h).to(dev)
+    ids = torch.empty(T, dtype=torch.int32, device=dev)
+    margin = torch.empty(T, dtype=torch.float32, device=dev)
+    n_acc = torch.empty(B, dtype=torch.int32, device=dev)
+    committed = torch.empty(B, K + 1, dtype=torch.int32, device=dev)
+    hidden_out = torch.empty_like(x) if wl.vocab == 0 else None
+
+    # Drafts that agree with the verifier's greedy choice with probability p: built from
+    # one untimed pass's argmax (the verifier's own choices, as a drafter would see them).
+    ctx.step(x, B, K, ids if wl.vocab else None, margin if wl.vocab else None, hidden_out)
+    torch.cuda.synchronize()
+    counts = ctx.expert_counts()
+    y0 = ids.cpu().numpy() if wl.vocab else np.zeros(T, np.int32)
+    drafts = torch.from_numpy(W.make_drafts(wl, y0)).to(dev) if K > 0 else torch.empty(B, 0, dtype=torch.int32,
+                                                                                        device=dev)
+
+    def step():
+        ctx.step(x, B, K, ids if wl.vocab else None, margin if wl.vocab else None, hidden_out)
+        if wl.vocab:
+            bnd.accept_greedy(drafts, ids, B, K, n_acc, committed)
+
+    # eager reference outputs, then (default) capture the step in a HIP graph
+    step()
+    torch.cuda.synchronize()
+    ref_ids, ref_n = ids.clone(), n_acc.clone()
+    mode = "eager"
+    run = step
+    if not args.eager:
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            step()  # warm the capture stream
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            step()
+        run = g.replay
+        mode = "hip_graph"
+        for _ in range(3):  # replays must reproduce the eager result exactly
+            ids.fill_(-1)
+            run()
+            torch.cuda.synchronize()
+            assert torch.equal(ids, ref_ids) and torch.equal(n_acc, ref_n), "graph replay differs from eager"
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+
+    # eager timing for reference (launch overhead visible)
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_eager = e0.elapsed_time(e1) / args.steps
+
+    # per-kernel durations from HIP events the library records around each launch
+    ctx.profile(True)
+    for _ in range(args.steps):
+        ctx.step(x, B, K, ids if wl.vocab else None, margin if wl.vocab else None, hidden_out)
+        prof = ctx.profile_read()
+    ctx.profile(False)
+
+    acc = algorithmic(wl, counts)
+    committed_per_step = int(n_acc.sum().item()) + B if wl.vocab else 0
+    per_kind = {k: {"avg_us": 1000.0 * v[0] / max(v[1], 1), "launches_per_step": v[1] / args.steps}
+                for k, v in prof.items()}
+    up_us = per_kind["gemm_up"]["avg_us"]
+    up_gbs = acc["up_bytes_per_launch"] / (up_us * 1e-6) / 1e9
+    step_gbs = acc["step_bytes"] / (ms * 1e-3) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline and wl.n_layers * wl.positions <= 12 * 512:
+        log("[bench] timing the CPU oracle on one pass")
+        cpu = cpu_baseline(wl, weights, x_h, lambda y: W.make_drafts(wl, y))
+
+    value = committed_per_step / (ms * 1e-3) if wl.vocab else T / (ms * 1e-3)
+    out = {
+        "metric": METRIC if wl.name == "decode_b32_k3" else f"verified tokens/sec per verify step ({wl.name})",
+        "value": round(value, 1),
+        "unit": "tokens/s" if wl.vocab else "positions/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.wdtype, "data": "synthetic",
+        "config": {"workload": wl.name, "B": B, "K": K, "blocks": wl.n_layers, "hidden": wl.hidden,
+                   "routed_experts": wl.n_routed, "top_k": wl.top_k, "shared_experts": wl.n_shared,
+                   "inter": wl.inter, "vocab": wl.vocab, "positions": T, "mode": mode},
+        "roofline": {"bound": "hbm", "kernel": "gemm_up (gate/up + SwiGLU)", "achieved": round(up_gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(up_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None},
+        "step_roofline": {"bound": "hbm", "achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": round(step_gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": acc["step_bytes"],
+                          "mfma_frac": round(acc["flops"] / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
+        "cpu_baseline": cpu,
+        "positions_per_s": round(T / (ms * 1e-3), 1),
+        "committed_per_step": committed_per_step,
+        "eager_ms_per_step": round(ms_eager, 4),
+        "kernels_us": {k: round(v["avg_us"], 2) for k, v in per_kind.items()},
+        "touched_experts_per_block": acc["touched_per_block"],
+    }
+    print(json.dumps(out), flush=True)
+    ctx.close()
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,453 @@
+// Host side of the C ABI declared in include/moe_verify.h.
+//
+// Every entry point checks its arguments on the host before any HIP call, reports
+// failures as status codes plus a thread-local message, and only enqueues work on the
+// caller's stream during a step (no allocation, synchronisation or host copy there).
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "launch.h"
+#include "moe_verify.h"
+
+#define MV_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return MOE_OK;
+}
+
+int elem_bytes(int32_t wdtype) { return wdtype == MOE_BF16 ? 2 : 4; }
+
+// Elements per 256-byte K block: the contraction granule of the packed GEMM layout.
+int kblock_elems(int32_t wdtype) { return mv::kRowBlockBytes / elem_bytes(wdtype); }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Upper bound on GEMM work items for T positions (each routed expert's rows split in
+// blocks of kGemmMB, plus at most one partial block per expert, plus the shared blocks).
+int64_t max_work_items(const moe_verify_config& c, int64_t T) {
+  const int64_t mb = mv::kGemmMB;
+  return (T * c.top_k + mb - 1) / mb + c.n_routed + (int64_t)c.n_shared * ((T + mb - 1) / mb);
+}
+
+int check_config(const moe_verify_config* c) {
+  if (!c) return fail(MOE_EINVAL, "config is NULL");
+  if (c->wdtype != MOE_F32 && c->wdtype != MOE_BF16) return fail(MOE_EINVAL, "wdtype %d is not MOE_F32 or MOE_BF16", c->wdtype);
+  if (c->hidden <= 0 || c->inter <= 0 || c->n_layers <= 0 || c->n_routed <= 0 || c->top_k <= 0 ||
+      c->n_shared < 0 || c->vocab < 0 || c->max_positions <= 0)
+    return fail(MOE_EINVAL, "config has a non-positive size (hidden %d inter %d layers %d routed %d top_k %d "
+                "shared %d vocab %d max_positions %d)", c->hidden, c->inter, c->n_layers, c->n_routed, c->top_k,
+                c->n_shared, c->vocab, c->max_positions);
+  if (!(c->rms_eps >= 0.0f)) return fail(MOE_EINVAL, "rms_eps must be >= 0");
+  if (c->n_routed > 64) return fail(MOE_EUNSUPPORTED, "n_routed %d > 64 (one wavefront lane per routed expert)", c->n_routed);
+  if (c->top_k > c->n_routed) return fail(MOE_EUNSUPPORTED, "top_k %d > n_routed %d", c->top_k, c->n_routed);
+  if (c->n_shared > 8) return fail(MOE_EUNSUPPORTED, "n_shared %d > 8", c->n_shared);
+  const int kb = kblock_elems(c->wdtype);
+  if (c->hidden % kb || c->inter % kb)
+    return fail(MOE_EUNSUPPORTED, "hidden %d and inter %d must be multiples of %d for this dtype", c->hidden,
+                c->inter, kb);
+  if (c->hidden > 4096 * (c->wdtype == MOE_BF16 ? 2 : 1) || c->inter > 16384)
+    return fail(MOE_EUNSUPPORTED, "hidden %d or inter %d too large", c->hidden, c->inter);
+  if (max_work_items(*c, c->max_positions) > 65535 || (int64_t)c->max_positions * c->top_k > (1ll << 30))
+    return fail(MOE_EUNSUPPORTED, "max_positions %d too large", c->max_positions);
+  return MOE_OK;
+}
+
+int check_step(const moe_verify_config* c, int32_t B, int32_t K, int has_in, int has_argmax, int has_hout) {
+  if (B < 1) return fail(MOE_EINVAL, "B = %d, need B >= 1", B);
+  if (K < 0) return fail(MOE_EINVAL, "K = %d, need K >= 0", K);
+  const int64_t T = (int64_t)B * (K + 1);
+  if (T > c->max_positions) return fail(MOE_EINVAL, "B*(K+1) = %lld exceeds max_positions %d", (long long)T, c->max_positions);
+  if (!has_in) return fail(MOE_EINVAL, "hidden_in is NULL");
+  if (c->vocab > 0 && !has_argmax) return fail(MOE_EINVAL, "argmax_out is required when vocab > 0");
+  if (c->vocab == 0 && has_argmax) return fail(MOE_EINVAL, "argmax_out given but the config has no LM head");
+  if (c->vocab == 0 && !has_hout) return fail(MOE_EINVAL, "hidden_out is required when vocab == 0");
+  return MOE_OK;
+}
+
+// Makes the context's device current for the scope of a call, restoring the caller's.
+struct DeviceGuard {
+  int prev = -1;
+  bool changed = false;
+  hipError_t err = hipSuccess;
+  explicit DeviceGuard(int dev) {
+    err = hipGetDevice(&prev);
+    if (err == hipSuccess && prev != dev) {
+      err = hipSetDevice(dev);
+      changed = err == hipSuccess;
+    }
+  }
+  ~DeviceGuard() {
+    if (changed) (void)hipSetDevice(prev);
+  }
+};
+
+}  // namespace
+
+struct moe_verify_ctx {
+  moe_verify_config cfg{};
+  int device = 0;
+  int es = 2;
+  int NQ_up = 0, NQ_dn = 0, NQ_lm = 0, n_pg_lm = 0, NKB_H = 0, NKB_I = 0;
+  size_t router_units_per_layer = 0, up_units_per_layer = 0, down_units_per_layer = 0;
+  // packed weights
+  uint4* router_p = nullptr;
+  float* bias_p = nullptr;  // [L][64]
+  uint4* up_p = nullptr;
+  uint4* down_p = nullptr;
+  uint4* lm_p = nullptr;
+  // workspace
+  float* x_ws = nullptr;
+  void* a = nullptr;
+  int32_t* topk_id = nullptr;
+  float* topk_w = nullptr;
+  int32_t* row_tok = nullptr;
+  int32_t* row_dst = nullptr;
+  float* row_gate = nullptr;
+  int4* work = nullptr;
+  int32_t* n_work = nullptr;
+  void* h = nullptr;
+  float* ybuf = nullptr;
+  mv::Top2* part = nullptr;
+  int32_t* counts = nullptr;  // [L][E] routed-slot count per expert, last step
+  std::vector<void*> allocs;
+  // profiling: one event pair per launch of the last step, and running totals
+  bool prof = false;
+  std::vector<hipEvent_t> ev;
+  std::vector<int> ev_kind;
+  int n_pairs = 0;
+  double prof_ms[MOE_PROF_KINDS] = {};
+  int64_t prof_n[MOE_PROF_KINDS] = {};
+
+  ~moe_verify_ctx() {
+    for (hipEvent_t e : ev) (void)hipEventDestroy(e);
+    for (void* p : allocs) (void)hipFree(p);
+  }
+  // Record the start event of a launch of class `kind` (no-op unless profiling).
+  void prof_begin(int kind, hipStream_t st) {
+    if (!prof || 2 * n_pairs + 1 >= (int)ev.size()) return;
+    ev_kind[n_pairs] = kind;
+    (void)hipEventRecord(ev[2 * n_pairs], st);
+  }
+  void prof_end(hipStream_t st) {
+    if (!prof || 2 * n_pairs + 1 >= (int)ev.size()) return;
+    (void)hipEventRecord(ev[2 * n_pairs + 1], st);
+    ++n_pairs;
+  }
+  template <typename P>
+  hipError_t alloc(P** out, size_t bytes) {
+    void* p = nullptr;
+    hipError_t e = hipMalloc(&p, bytes < 256 ? 256 : bytes);
+    if (e != hipSuccess) return e;
+    allocs.push_back(p);
+    *out = static_cast<P*>(p);
+    return hipSuccess;
+  }
+};
+
+namespace {
+
+#define MV_CHECK(call)                                                                          \
+  do {                                                                                          \
+    hipError_t e_ = (call);                                                                     \
+    if (e_ != hipSuccess) return fail(MOE_EDEVICE, "%s: %s", #call, hipGetErrorString(e_));     \
+  } while (0)
+
+// Launch the MoE block `l` over Tn positions whose residual input is x_in (plus the
+// previous block's ybuf when given). Leaves the block's per-slot outputs in ybuf.
+int run_block(moe_verify_ctx* c, int l, const float* x_in, const float* ybuf_prev, int Tn, hipStream_t st) {
+  const moe_verify_config& g = c->cfg;
+  const int E = g.n_routed, S = g.n_shared, k = g.top_k, KS = k + S, H = g.hidden, I = g.inter;
+  c->prof_begin(MOE_PROF_NORM_ROUTE, st);
+  MV_CHECK(mv::launch_norm_route(g.wdtype, true, x_in, ybuf_prev, c->x_ws, nullptr, c->a,
+                                 c->router_p + l * c->router_units_per_layer, c->bias_p + (size_t)l * 64, c->topk_id,
+                                 c->topk_w, Tn, H, KS, E, k, g.rms_eps, st));
+  c->prof_end(st);
+  c->prof_begin(MOE_PROF_PLAN, st);
+  MV_CHECK(mv::launch_plan(c->topk_id, c->topk_w, Tn, k, E, S, c->row_tok, c->row_dst, c->row_gate, c->work,
+                           c->n_work, c->counts + (size_t)l * E, st));
+  c->prof_end(st);
+  const int wmax = (int)max_work_items(g, Tn);
+  mv::GemmArgs a{};
+  a.work = c->work;
+  a.n_work = c->n_work;
+  a.Tn = Tn;
+  a.k = k; a.E = E; a.KS = KS; a.H = H; a.I = I;
+  a.row_tok = c->row_tok;
+  a.row_dst = c->row_dst;
+  a.row_gate = c->row_gate;
+  // gate/up + SwiGLU
+  a.A = c->a;
+  a.B = c->up_p + l * c->up_units_per_layer;
+  a.K = H;
+  a.NQ = c->NQ_up;
+  a.h = c->h;
+  c->prof_begin(MOE_PROF_GEMM_UP, st);
+  MV_CHECK(mv::launch_gemm(g.wdtype, mv::EPI_UP, a, dim3((c->NQ_up + mv::kGemmWaves - 1) / mv::kGemmWaves, wmax), st));
+  c->prof_end(st);
+  // down + gate scale
+  a.A = c->h;
+  a.B = c->down_p + l * c->down_units_per_layer;
+  a.K = I;
+  a.NQ = c->NQ_dn;
+  a.ybuf = c->ybuf;
+  c->prof_begin(MOE_PROF_GEMM_DOWN, st);
+  MV_CHECK(mv::launch_gemm(g.wdtype, mv::EPI_DOWN, a, dim3((c->NQ_dn + mv::kGemmWaves - 1) / mv::kGemmWaves, wmax), st));
+  c->prof_end(st);
+  return MOE_OK;
+}
+
+}  // namespace
+
+MV_API int moe_verify_check_config(const moe_verify_config* cfg) {
+  const int rc = check_config(cfg);
+  return rc ? rc : ok();
+}
+
+MV_API int moe_verify_check_step(const moe_verify_config* cfg, int32_t B, int32_t K, int has_hidden_in,
+                                 int has_argmax, int has_hidden_out) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  rc = check_step(cfg, B, K, has_hidden_in, has_argmax, has_hidden_out);
+  return rc ? rc : ok();
+}
+
+MV_API const char* moe_verify_last_error(void) { return g_last_error.c_str(); }
+
+MV_API int moe_verify_init(const moe_verify_config* cfg, const moe_verify_weights* w, void* stream,
+                           moe_verify_ctx** out) {
+  if (!out) return fail(MOE_EINVAL, "out is NULL");
+  *out = nullptr;
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (!w) return fail(MOE_EINVAL, "weights is NULL");
+  if (!w->router_w || !w->w_gate || !w->w_up || !w->w_down) return fail(MOE_EINVAL, "a required weight pointer is NULL");
+  if ((cfg->vocab > 0) != (w->lm_head != nullptr)) return fail(MOE_EINVAL, "lm_head must be non-NULL iff vocab > 0");
+  if (!aligned16(w->router_w) || !aligned16(w->w_gate) || !aligned16(w->w_up) || !aligned16(w->w_down) ||
+      (w->lm_head && !aligned16(w->lm_head)))
+    return fail(MOE_EINVAL, "weight pointers must be 16-byte aligned");
+
+  const moe_verify_config& g = *cfg;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  moe_verify_ctx* c = new (std::nothrow) moe_verify_ctx();
+  if (!c) return fail(MOE_ENOMEM, "host allocation failed");
+  c->cfg = g;
+  c->es = elem_bytes(g.wdtype);
+  hipError_t he = hipGetDevice(&c->device);
+  if (he != hipSuccess) {
+    delete c;
+    return fail(MOE_EDEVICE, "hipGetDevice: %s", hipGetErrorString(he));
+  }
+  const int E = g.n_routed, S = g.n_shared, k = g.top_k, KS = k + S, H = g.hidden, I = g.inter, L = g.n_layers;
+  const size_t es = c->es, P = (size_t)g.max_positions;
+  c->NKB_H = (int)(H * es / mv::kRowBlockBytes);
+  c->NKB_I = (int)(I * es / mv::kRowBlockBytes);
+  c->NQ_up = I / 16;
+  c->NQ_dn = (H + 31) / 32;
+  c->NQ_lm = (g.vocab + 31) / 32;
+  c->n_pg_lm = (c->NQ_lm + mv::kGemmWaves - 1) / mv::kGemmWaves;
+  c->router_units_per_layer = (size_t)(H * es / 16) * 64;
+  c->up_units_per_layer = (size_t)(E + S) * c->NQ_up * c->NKB_H * mv::kPairUnits;
+  c->down_units_per_layer = (size_t)(E + S) * c->NQ_dn * c->NKB_I * mv::kPairUnits;
+  const size_t lm_units = (size_t)c->NQ_lm * c->NKB_H * mv::kPairUnits;
+  const size_t wmax = (size_t)max_work_items(g, g.max_positions);
+
+  hipError_t ae = hipSuccess;
+  auto A = [&](auto** p, size_t bytes) {
+    if (ae == hipSuccess) ae = c->alloc(p, bytes);
+  };
+  A(&c->router_p, c->router_units_per_layer * L * 16);
+  A(&c->bias_p, (size_t)L * 64 * sizeof(float));
+  A(&c->up_p, c->up_units_per_layer * L * 16);
+  A(&c->down_p, c->down_units_per_layer * L * 16);
+  if (g.vocab > 0) A(&c->lm_p, lm_units * 16);
+  A(&c->x_ws, P * H * sizeof(float));
+  A(&c->a, P * H * es);
+  A(&c->topk_id, P * k * sizeof(int32_t));
+  A(&c->topk_w, P * k * sizeof(float));
+  A(&c->row_tok, P * k * sizeof(int32_t));
+  A(&c->row_dst, P * k * sizeof(int32_t));
+  A(&c->row_gate, P * k * sizeof(float));
+  A(&c->work, wmax * sizeof(int4));
+  A(&c->n_work, sizeof(int32_t));
+  A(&c->h, P * KS * I * es);
+  A(&c->ybuf, P * KS * H * sizeof(float));
+  if (g.vocab > 0) A(&c->part, P * c->n_pg_lm * sizeof(mv::Top2));
+  A(&c->counts, (size_t)L * E * sizeof(int32_t));
+  if (ae != hipSuccess) {
+    delete c;
+    (void)hipGetLastError();
+    return fail(MOE_ENOMEM, "device allocation failed: %s", hipGetErrorString(ae));
+  }
+
+  auto bail = [&](hipError_t e, const char* what) {
+    delete c;
+    return fail(MOE_EDEVICE, "%s: %s", what, hipGetErrorString(e));
+  };
+  const size_t row_h = H * es, row_i = I * es;
+  if ((he = mv::launch_repack_router(w->router_w, c->router_p, L, E, (int)row_h, st)) != hipSuccess)
+    return bail(he, "router repack");
+  if ((he = hipMemsetAsync(c->bias_p, 0, (size_t)L * 64 * sizeof(float), st)) != hipSuccess) return bail(he, "bias clear");
+  if (w->router_bias &&
+      (he = hipMemcpy2DAsync(c->bias_p, 64 * sizeof(float), w->router_bias, E * sizeof(float), E * sizeof(float), L,
+                             hipMemcpyDeviceToDevice, st)) != hipSuccess)
+    return bail(he, "bias copy");
+  // gate/up: pair q = (gate tile q, up tile q); matrices are the L*(E+S) experts
+  if ((he = mv::launch_repack_pairs(w->w_gate, w->w_up, c->up_p, L * (E + S), I, (int)row_h, c->NQ_up, c->NKB_H, 1,
+                                    (size_t)I * row_h, st)) != hipSuccess)
+    return bail(he, "gate/up repack");
+  if ((he = mv::launch_repack_pairs(w->w_down, w->w_down, c->down_p, L * (E + S), H, (int)row_i, c->NQ_dn, c->NKB_I, 0,
+                                    (size_t)H * row_i, st)) != hipSuccess)
+    return bail(he, "down repack");
+  if (g.vocab > 0 &&
+      (he = mv::launch_repack_pairs(w->lm_head, w->lm_head, c->lm_p, 1, g.vocab, (int)row_h, c->NQ_lm, c->NKB_H, 0,
+                                    (size_t)g.vocab * row_h, st)) != hipSuccess)
+    return bail(he, "lm_head repack");
+  if ((he = hipStreamSynchronize(st)) != hipSuccess) return bail(he, "repack");
+  *out = c;
+  return ok();
+}
+
+MV_API int moe_verify_step(moe_verify_ctx* c, const float* hidden_in, int32_t B, int32_t K, int32_t* argmax_out,
+                           float* margin_out, float* hidden_out, void* stream) {
+  if (!c) return fail(MOE_EINVAL, "context is NULL");
+  int rc = check_step(&c->cfg, B, K, hidden_in != nullptr, argmax_out != nullptr, hidden_out != nullptr);
+  if (rc) return rc;
+  const moe_verify_config& g = c->cfg;
+  const int Tn = B * (K + 1);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  DeviceGuard dg(c->device);
+  if (dg.err != hipSuccess) return fail(MOE_EDEVICE, "device select: %s", hipGetErrorString(dg.err));
+  c->n_pairs = 0;
+  for (int l = 0; l < g.n_layers; ++l) {
+    rc = run_block(c, l, l == 0 ? hidden_in : c->x_ws, l == 0 ? nullptr : c->ybuf, Tn, st);
+    if (rc) return rc;
+  }
+  const int KS = g.top_k + g.n_shared;
+  c->prof_begin(MOE_PROF_NORM_ROUTE, st);
+  MV_CHECK(mv::launch_norm_route(g.wdtype, false, c->x_ws, c->ybuf, nullptr, hidden_out, c->a, nullptr, nullptr,
+                                 nullptr, nullptr, Tn, g.hidden, KS, g.n_routed, g.top_k, g.rms_eps, st));
+  c->prof_end(st);
+  if (g.vocab > 0) {
+    mv::GemmArgs a{};
+    a.A = c->a;
+    a.B = c->lm_p;
+    a.K = g.hidden;
+    a.NQ = c->NQ_lm;
+    a.n_valid = g.vocab;
+    a.Tn = Tn;
+    a.part = c->part;
+    a.n_pg = c->n_pg_lm;
+    c->prof_begin(MOE_PROF_LM_HEAD, st);
+    MV_CHECK(mv::launch_gemm(g.wdtype, mv::EPI_LM, a, dim3(c->n_pg_lm, (Tn + mv::kGemmMB - 1) / mv::kGemmMB), st));
+    c->prof_end(st);
+    c->prof_begin(MOE_PROF_ARGMAX, st);
+    MV_CHECK(mv::launch_argmax_reduce(c->part, c->n_pg_lm, Tn, argmax_out, margin_out, st));
+    c->prof_end(st);
+  }
+  return ok();
+}
+
+MV_API int accept_greedy(const int32_t* draft_ids, const int32_t* argmax_ids, int32_t B, int32_t K,
+                         int32_t* accepted_len, int32_t* committed, void* stream) {
+  if (B < 1) return fail(MOE_EINVAL, "B = %d, need B >= 1", B);
+  if (K < 0) return fail(MOE_EINVAL, "K = %d, need K >= 0", K);
+  if ((K > 0 && !draft_ids) || !argmax_ids || !accepted_len || !committed)
+    return fail(MOE_EINVAL, "a required pointer is NULL");
+  MV_CHECK(mv::launch_accept(draft_ids, argmax_ids, B, K, accepted_len, committed, static_cast<hipStream_t>(stream)));
+  return ok();
+}
+
+MV_API int moe_verify_debug_layer(moe_verify_ctx* c, int32_t layer, const float* x_in, int32_t T, float* moe_out,
+                                  int32_t* topk_id, float* topk_w, void* stream) {
+  if (!c) return fail(MOE_EINVAL, "context is NULL");
+  const moe_verify_config& g = c->cfg;
+  if (layer < 0 || layer >= g.n_layers) return fail(MOE_EINVAL, "layer %d out of range [0, %d)", layer, g.n_layers);
+  if (T < 1 || T > g.max_positions) return fail(MOE_EINVAL, "T = %d out of range [1, %d]", T, g.max_positions);
+  if (!x_in) return fail(MOE_EINVAL, "x_in is NULL");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  DeviceGuard dg(c->device);
+  if (dg.err != hipSuccess) return fail(MOE_EDEVICE, "device select: %s", hipGetErrorString(dg.err));
+  int rc = run_block(c, layer, x_in, nullptr, T, st);
+  if (rc) return rc;
+  const int KS = g.top_k + g.n_shared;
+  if (moe_out) MV_CHECK(mv::launch_combine(c->ybuf, T, g.hidden, KS, moe_out, st));
+  const size_t kb = (size_t)T * g.top_k * 4;
+  if (topk_id) MV_CHECK(hipMemcpyAsync(topk_id, c->topk_id, kb, hipMemcpyDeviceToDevice, st));
+  if (topk_w) MV_CHECK(hipMemcpyAsync(topk_w, c->topk_w, kb, hipMemcpyDeviceToDevice, st));
+  return ok();
+}
+
+MV_API void moe_verify_destroy(moe_verify_ctx* c) {
+  if (!c) return;
+  DeviceGuard dg(c->device);
+  (void)hipDeviceSynchronize();
+  delete c;
+}
+
+MV_API int moe_verify_profile(moe_verify_ctx* c, int enable) {
+  if (!c) return fail(MOE_EINVAL, "context is NULL");
+  DeviceGuard dg(c->device);
+  if (dg.err != hipSuccess) return fail(MOE_EDEVICE, "device select: %s", hipGetErrorString(dg.err));
+  const size_t need = 2 * (size_t)(4 * c->cfg.n_layers + 3);
+  while (enable && c->ev.size() < need) {
+    hipEvent_t e;
+    MV_CHECK(hipEventCreate(&e));
+    c->ev.push_back(e);
+  }
+  c->ev_kind.assign(c->ev.size() / 2 + 1, 0);
+  c->prof = enable != 0;
+  c->n_pairs = 0;
+  for (int i = 0; i < MOE_PROF_KINDS; ++i) {
+    c->prof_ms[i] = 0.0;
+    c->prof_n[i] = 0;
+  }
+  return ok();
+}
+
+MV_API int moe_verify_profile_read(moe_verify_ctx* c, double* ms, int64_t* launches) {
+  if (!c) return fail(MOE_EINVAL, "context is NULL");
+  DeviceGuard dg(c->device);
+  if (dg.err != hipSuccess) return fail(MOE_EDEVICE, "device select: %s", hipGetErrorString(dg.err));
+  if (c->n_pairs > 0) MV_CHECK(hipEventSynchronize(c->ev[2 * c->n_pairs - 1]));
+  for (int i = 0; i < c->n_pairs; ++i) {
+    float t = 0.f;
+    MV_CHECK(hipEventElapsedTime(&t, c->ev[2 * i], c->ev[2 * i + 1]));
+    c->prof_ms[c->ev_kind[i]] += t;
+    c->prof_n[c->ev_kind[i]] += 1;
+  }
+  c->n_pairs = 0;
+  for (int i = 0; i < MOE_PROF_KINDS; ++i) {
+    if (ms) ms[i] = c->prof_ms[i];
+    if (launches) launches[i] = c->prof_n[i];
+  }
+  return ok();
+}
+
+MV_API int moe_verify_expert_counts(moe_verify_ctx* c, int32_t* counts) {
+  if (!c) return fail(MOE_EINVAL, "context is NULL");
+  if (!counts) return fail(MOE_EINVAL, "counts is NULL");
+  DeviceGuard dg(c->device);
+  if (dg.err != hipSuccess) return fail(MOE_EDEVICE, "device select: %s", hipGetErrorString(dg.err));
+  MV_CHECK(hipDeviceSynchronize());
+  MV_CHECK(hipMemcpy(counts, c->counts, (size_t)c->cfg.n_layers * c->cfg.n_routed * sizeof(int32_t),
+                     hipMemcpyDeviceToHost));
+  return ok();
+}

@@ -1,0 +1,101 @@
+// Device helpers shared by the gfx950 kernels of the verify step.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mv {
+
+constexpr int kWave = 64;           // CDNA wavefront width
+constexpr int kRowBlockBytes = 256; // bytes of one row per K block of the packed GEMM layout
+constexpr int kChunksPerRow = kRowBlockBytes / 16;  // 16-byte chunks per row per K block
+constexpr int kPairUnits = 2 * 4 * kWave;           // 16-byte units per (pair, K block) = 8 KB
+constexpr int kGemmWaves = 4;                       // waves per GEMM workgroup (one pair each)
+constexpr int kGemmMB = 64;                         // rows per GEMM work item (max M per pass)
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// bf16 is carried as uint16_t bit patterns.
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// float32 -> bf16 bit pattern, round to nearest, ties to even (inputs are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static constexpr int per16 = 4;  // elements per 16-byte chunk
+  __device__ static __forceinline__ float load(const float* p, int i) { return p[i]; }
+};
+template <> struct Elem<uint16_t> {
+  static constexpr int per16 = 8;
+  __device__ static __forceinline__ float load(const uint16_t* p, int i) { return bf16_to_f32(p[i]); }
+};
+
+// Store a float32 value as the element type (bf16 rounding or plain float).
+__device__ __forceinline__ void store_elem(float* p, size_t i, float v) { p[i] = v; }
+__device__ __forceinline__ void store_elem(uint16_t* p, size_t i, float v) { p[i] = (uint16_t)f32_to_bf16(v); }
+
+// acc += A_chunk * B_chunk over one 16-byte chunk per lane.
+// Lane l holds row (l % 16) of A and column (l % 16) of B; the four lane groups
+// (l / 16) hold disjoint K slices, identically placed in A and B, so the sum covers
+// every K element of the chunk exactly once whatever the K order inside the MFMA.
+// The 16x16 result: lane l holds column (l % 16), rows 4*(l/16) + 0..3.
+__device__ __forceinline__ void mma_chunk(f32x4_t& acc, uint4 a, uint4 b, uint16_t*) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma_chunk(f32x4_t& acc, uint4 a, uint4 b, float*) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
+}
+
+// Streaming (read-once) 16-byte load: non-temporal, so the weight stream does not
+// evict the small, re-used activation rows from the caches.
+__device__ __forceinline__ uint4 load_stream(const uint4* p) {
+  u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Top-1/top-2 record for the argmax reductions: value, lowest index, second value.
+struct Top2 {
+  float v1;
+  int i1;
+  float v2;
+};
+
+// Merge two records: the larger value wins, the lower index on equal values; the
+// loser's best competes for second place. Commutative and associative.
+__device__ __forceinline__ Top2 top2_merge(Top2 a, Top2 b) {
+  const bool b_wins = (b.v1 > a.v1) || (b.v1 == a.v1 && b.i1 < a.i1);
+  Top2 r;
+  if (b_wins) {
+    r.v1 = b.v1; r.i1 = b.i1; r.v2 = fmaxf(b.v2, a.v1);
+  } else {
+    r.v1 = a.v1; r.i1 = a.i1; r.v2 = fmaxf(a.v2, b.v1);
+  }
+  return r;
+}
+
+__device__ __forceinline__ Top2 top2_shfl_xor(Top2 t, int mask) {
+  Top2 o;
+  o.v1 = __shfl_xor(t.v1, mask, kWave);
+  o.i1 = __shfl_xor(t.i1, mask, kWave);
+  o.v2 = __shfl_xor(t.v2, mask, kWave);
+  return o;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
+}  // namespace mv

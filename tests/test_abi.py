@@ -1,0 +1,133 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad arguments on
+the host before touching a device (CPU only: none of these calls reaches HIP)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from lossless_speculative_verification_amd import binding as bnd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_verify.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w]*\s*\**\s*([A-Za-z_]\w*)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "while")))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bnd.LIB_PATH):
+        import __graft_entry__
+
+        __graft_entry__.build()
+    return bnd.load_library()
+
+
+def _cfg(**kw):
+    base = dict(hidden=128, n_routed=8, top_k=2, n_shared=1, inter=64, n_layers=1, vocab=1000, wdtype=bnd.MOE_F32,
+                rms_eps=1e-6, max_positions=16)
+    base.update(kw)
+    return bnd.Config(**base)
+
+
+def test_header_declares_the_expected_calls():
+    assert set(_declared_functions()) == set(bnd.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_valid_configs_pass(lib):
+    assert lib.moe_verify_check_config(ctypes.byref(_cfg())) == bnd.MOE_OK
+    real = _cfg(hidden=1280, n_routed=64, top_k=6, n_shared=2, inter=896, n_layers=12, vocab=129280,
+                wdtype=bnd.MOE_BF16, max_positions=36992)
+    assert lib.moe_verify_check_config(ctypes.byref(real)) == bnd.MOE_OK
+    assert bnd.last_error() == ""
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(hidden=0), bnd.MOE_EINVAL),
+    (dict(inter=-64), bnd.MOE_EINVAL),
+    (dict(n_layers=0), bnd.MOE_EINVAL),
+    (dict(top_k=0), bnd.MOE_EINVAL),
+    (dict(n_shared=-1), bnd.MOE_EINVAL),
+    (dict(vocab=-1), bnd.MOE_EINVAL),
+    (dict(max_positions=0), bnd.MOE_EINVAL),
+    (dict(wdtype=7), bnd.MOE_EINVAL),
+    (dict(rms_eps=-1.0), bnd.MOE_EINVAL),
+    (dict(n_routed=65, top_k=2), bnd.MOE_EUNSUPPORTED),
+    (dict(top_k=9), bnd.MOE_EUNSUPPORTED),
+    (dict(n_shared=9), bnd.MOE_EUNSUPPORTED),
+    (dict(hidden=100), bnd.MOE_EUNSUPPORTED),
+    (dict(inter=96), bnd.MOE_EUNSUPPORTED),
+    (dict(hidden=192, wdtype=bnd.MOE_BF16), bnd.MOE_EUNSUPPORTED),
+    (dict(max_positions=10_000_000), bnd.MOE_EUNSUPPORTED),
+])
+def test_bad_configs_rejected(lib, kw, code):
+    assert lib.moe_verify_check_config(ctypes.byref(_cfg(**kw))) == code
+    assert bnd.last_error() != ""
+
+
+def test_null_config_rejected(lib):
+    assert lib.moe_verify_check_config(None) == bnd.MOE_EINVAL
+
+
+@pytest.mark.parametrize("B,K,has_in,has_arg,has_out,vocab,code", [
+    (1, 3, 1, 1, 0, 1000, bnd.MOE_OK),
+    (4, 3, 1, 1, 1, 1000, bnd.MOE_OK),
+    (16, 0, 1, 1, 0, 1000, bnd.MOE_OK),   # T == max_positions, speculation off
+    (0, 3, 1, 1, 0, 1000, bnd.MOE_EINVAL),
+    (1, -1, 1, 1, 0, 1000, bnd.MOE_EINVAL),
+    (5, 3, 1, 1, 0, 1000, bnd.MOE_EINVAL),  # 20 positions > 16
+    (1, 3, 0, 1, 0, 1000, bnd.MOE_EINVAL),
+    (1, 3, 1, 0, 0, 1000, bnd.MOE_EINVAL),  # argmax required with an LM head
+    (1, 3, 1, 1, 1, 0, bnd.MOE_EINVAL),     # argmax given without an LM head
+    (1, 3, 1, 0, 0, 0, bnd.MOE_EINVAL),     # hidden_out required without an LM head
+    (1, 3, 1, 0, 1, 0, bnd.MOE_OK),
+])
+def test_step_argument_checks(lib, B, K, has_in, has_arg, has_out, vocab, code):
+    cfg = _cfg(vocab=vocab)
+    assert lib.moe_verify_check_step(ctypes.byref(cfg), B, K, has_in, has_arg, has_out) == code
+
+
+def test_entry_points_reject_before_any_device_call(lib):
+    out = ctypes.c_void_p(123)
+    w = bnd.WeightPtrs()
+    # invalid config: rejected and *out cleared
+    assert lib.moe_verify_init(ctypes.byref(_cfg(hidden=0)), ctypes.byref(w), None, ctypes.byref(out)) == bnd.MOE_EINVAL
+    assert out.value is None
+    # valid config, NULL weights
+    assert lib.moe_verify_init(ctypes.byref(_cfg()), None, None, ctypes.byref(out)) == bnd.MOE_EINVAL
+    assert lib.moe_verify_init(ctypes.byref(_cfg()), ctypes.byref(w), None, ctypes.byref(out)) == bnd.MOE_EINVAL
+    # lm_head given although vocab == 0 / misaligned pointers
+    w2 = bnd.WeightPtrs(16, None, 16, 16, 16, 16)
+    assert lib.moe_verify_init(ctypes.byref(_cfg(vocab=0)), ctypes.byref(w2), None, ctypes.byref(out)) == bnd.MOE_EINVAL
+    w3 = bnd.WeightPtrs(17, None, 16, 16, 16, 16)
+    assert lib.moe_verify_init(ctypes.byref(_cfg()), ctypes.byref(w3), None, ctypes.byref(out)) == bnd.MOE_EINVAL
+    assert "aligned" in bnd.last_error()
+    assert lib.moe_verify_init(ctypes.byref(_cfg()), ctypes.byref(w), None, None) == bnd.MOE_EINVAL
+    # null context
+    assert lib.moe_verify_step(None, 16, 1, 3, 16, None, None, None) == bnd.MOE_EINVAL
+    assert lib.moe_verify_debug_layer(None, 0, 16, 4, None, None, None, None) == bnd.MOE_EINVAL
+    # acceptance
+    assert lib.accept_greedy(16, 16, 0, 3, 16, 16, None) == bnd.MOE_EINVAL
+    assert lib.accept_greedy(16, 16, 1, -1, 16, 16, None) == bnd.MOE_EINVAL
+    assert lib.accept_greedy(None, 16, 1, 3, 16, 16, None) == bnd.MOE_EINVAL
+    assert lib.accept_greedy(16, None, 1, 3, 16, 16, None) == bnd.MOE_EINVAL
+    assert lib.accept_greedy(16, 16, 1, 3, None, 16, None) == bnd.MOE_EINVAL
+    assert "NULL" in bnd.last_error()
+    lib.moe_verify_destroy(None)  # no-op
+
+
+def test_binding_raises_with_message(lib):
+    with pytest.raises(bnd.MoeVerifyError) as ei:
+        bnd._check(lib.moe_verify_check_config(ctypes.byref(_cfg(top_k=9))), "check")
+    assert ei.value.code == bnd.MOE_EUNSUPPORTED and "top_k" in str(ei.value)

@@ -1,0 +1,282 @@
+"""GPU parity of the HIP verify path against the CPU oracle, through the C ABI.
+
+Every case prints its name and shape before touching the GPU. Inputs are the seeded
+synthetic workloads; expected values come only from the oracle on the same inputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from lossless_speculative_verification_amd import binding as bnd
+from lossless_speculative_verification_amd import workload as W
+
+from gpu_cases import (DEV, GATE, TOL, context, decisive_positions, log, oracle_step, row_rel_err, run_debug_layer,
+                       run_step)
+
+pytestmark = pytest.mark.gpu
+
+WL = W.WORKLOADS
+
+
+# ----------------------------------------------------------------------------- acceptance kernel
+
+
+@pytest.mark.parametrize("B,K", [(1, 0), (1, 1), (3, 2), (32, 3), (129, 5), (1000, 3)])
+def test_accept_kernel_bit_exact(B, K):
+    log(f"[accept] B={B} K={K}")
+    rng = np.random.default_rng(B * 100 + K)
+    y = rng.integers(0, 50, (B, K + 1)).astype(np.int32)
+    d = np.where(rng.random((B, K)) < 0.7, y[:, :K], rng.integers(-3, 50, (B, K))).astype(np.int32)
+    n_ref, c_ref = O.accept(d, y, B, K)
+    dd, yd = torch.from_numpy(d).to(DEV), torch.from_numpy(y).to(DEV)
+    n = torch.full((B,), -9, dtype=torch.int32, device=DEV)
+    c = torch.full((B, K + 1), -9, dtype=torch.int32, device=DEV)
+    bnd.accept_greedy(dd, yd, B, K, n, c)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(n.cpu().numpy(), n_ref)
+    np.testing.assert_array_equal(c.cpu().numpy(), c_ref)
+
+
+# ----------------------------------------------------------------------------- full step checks
+
+
+def _check_step(wl, ref, ids, margin, hout, x, rows=None, min_decisive=1):
+    """Compare a GPU pass (restricted to `rows` when the oracle ran on a sample)."""
+    sel = slice(None) if rows is None else list(rows)
+    tol = TOL[wl.wdtype]
+    dec = decisive_positions(ref)
+    assert dec.sum() >= min_decisive, f"only {dec.sum()} decisive positions"
+    m_gpu = hout[sel].astype(np.float64) - x[sel]
+    m_ref = ref["hidden_out"].astype(np.float64) - x[sel]
+    err = row_rel_err(m_gpu[dec], m_ref[dec])
+    log(f"  decisive {dec.sum()}/{len(dec)}  hidden rel err {err:.3e} (tol {tol})")
+    assert err <= tol
+    if wl.vocab > 0:
+        np.testing.assert_array_equal(ids[sel][dec], ref["ids"][dec])
+        assert np.all(ids >= 0) and np.all(ids < wl.vocab)
+        dm = np.abs(margin[sel][dec] - ref["margin"][dec]).max()
+        log(f"  argmax exact on decisive; margin max abs diff {dm:.2e}")
+        assert dm < (1e-4 if wl.wdtype == "f32" else 2e-2)
+    return dec
+
+
+def _check_accept(wl, ref_ids, gpu_ids, dec):
+    """Accept on the GPU with drafts built from the oracle's choices; exact on sequences
+    whose positions are all decisive."""
+    B, K = wl.batch, wl.drafts
+    drafts = W.make_drafts(wl, ref_ids)
+    n_ref, c_ref = O.accept(drafts, ref_ids, B, K)
+    dd = torch.from_numpy(drafts).to(DEV)
+    yd = torch.from_numpy(gpu_ids.astype(np.int32)).to(DEV)
+    n = torch.empty(B, dtype=torch.int32, device=DEV)
+    c = torch.empty(B, K + 1, dtype=torch.int32, device=DEV)
+    bnd.accept_greedy(dd, yd, B, K, n, c)
+    torch.cuda.synchronize()
+    seq_ok = dec.reshape(B, K + 1).all(axis=1)
+    np.testing.assert_array_equal(n.cpu().numpy()[seq_ok], n_ref[seq_ok])
+    np.testing.assert_array_equal(c.cpu().numpy()[seq_ok], c_ref[seq_ok])
+    log(f"  accept exact on {seq_ok.sum()}/{B} sequences; mean accepted {n_ref.mean():.3f}")
+
+
+def test_tiny_fp32_step():
+    wl = WL["tiny_fp32"]
+    x = W.make_hidden(wl)
+    ref = oracle_step(wl)
+    ids, margin, hout = run_step(wl)
+    dec = _check_step(wl, ref, ids, margin, hout, x)
+    _check_accept(wl, ref["ids"], ids, dec)
+
+
+@pytest.mark.parametrize("B,K", [(1, 0), (67, 0), (16, 3), (9, 7)])
+def test_tiny_fp32_shapes(B, K):
+    """T = 1, a ragged T spanning several 16-row tiles and two work items per expert,
+    the capacity limit, and a long draft block."""
+    wl = WL["tiny_fp32"].with_(batch=B, drafts=K)
+    x = W.make_hidden(wl)
+    ref = O.verify_step(wl, W.make_weights(wl), x)
+    ids, margin, hout = run_step(wl, x, B, K)
+    _check_step(wl, ref, ids, margin, hout, x)
+
+
+def test_tiny_fp32_debug_layer():
+    wl = WL["tiny_fp32"]
+    x = W.make_hidden(wl, 200)
+    ref = O.moe_layer(wl, W.make_weights(wl), 0, x)
+    m, tid, tw = run_debug_layer(wl, 0, x)
+    dec = ref["gap"] > GATE
+    np.testing.assert_array_equal(tid[dec], ref["ids"][dec])
+    assert np.abs(tw[dec] - ref["gates"][dec]).max() < 1e-5
+    np.testing.assert_allclose(tw.sum(axis=1), 1.0, atol=1e-5)
+    err = row_rel_err(m[dec], ref["m"][dec])
+    log(f"  decisive {dec.sum()}/200 m rel err {err:.2e}")
+    assert err <= TOL["f32"]
+
+
+def test_layer1_bf16_step():
+    wl = WL["layer1_bf16"]
+    x = W.make_hidden(wl)
+    ref = oracle_step(wl)
+    ids, margin, hout = run_step(wl)
+    dec = _check_step(wl, ref, ids, margin, hout, x, min_decisive=0)
+    _check_accept(wl, ref["ids"], ids, dec)
+
+
+def test_layer1_bf16_speculation_off():
+    wl = WL["layer1_bf16"].with_(drafts=0)
+    from gpu_cases import host_weights
+    x = W.make_hidden(wl)
+    ref = O.verify_step(wl, host_weights(wl), x)
+    ids, margin, hout = run_step(wl, x, 1, 0)
+    _check_step(wl, ref, ids, margin, hout, x, min_decisive=0)
+
+
+def test_layer1_bf16_debug_layer_256_positions():
+    wl = WL["layer1_bf16"]
+    from gpu_cases import host_weights
+    x = W.make_hidden(wl, 256)
+    ref = O.moe_layer(wl, host_weights(wl), 0, x)
+    m, tid, tw = run_debug_layer(wl, 0, x)
+    dec = ref["gap"] > GATE
+    assert dec.sum() > 150
+    np.testing.assert_array_equal(tid[dec], ref["ids"][dec])
+    assert np.abs(tw[dec] - ref["gates"][dec]).max() < 1e-3
+    err = row_rel_err(m[dec], ref["m"][dec])
+    log(f"  decisive {dec.sum()}/256 m rel err {err:.2e}")
+    assert err <= TOL["bf16"]
+
+
+# ----------------------------------------------------------------------------- 12-layer decode
+
+
+@pytest.mark.parametrize("name", ["decode_b32_k3", "decode_b32_k1"])
+def test_decode_step(name):
+    wl = WL[name]
+    x = W.make_hidden(wl)
+    ref = oracle_step(wl)
+    ids, margin, hout = run_step(wl)
+    dec = _check_step(wl, ref, ids, margin, hout, x, min_decisive=5)
+    _check_accept(wl, ref["ids"], ids, dec)
+
+
+@pytest.mark.parametrize("layer", [0, 5, 11])
+def test_decode_debug_layer(layer):
+    wl = WL["decode_b32_k3"]
+    from gpu_cases import host_weights
+    x = W.make_hidden(wl)
+    ref = O.moe_layer(wl, host_weights(wl), layer, x)
+    m, tid, tw = run_debug_layer(wl, layer, x)
+    dec = ref["gap"] > GATE
+    np.testing.assert_array_equal(tid[dec], ref["ids"][dec])
+    err = row_rel_err(m[dec], ref["m"][dec])
+    log(f"  layer {layer}: decisive {dec.sum()}/128 m rel err {err:.2e}")
+    assert err <= TOL["bf16"]
+
+
+def test_decode_deterministic_and_batch_invariant():
+    wl = WL["decode_b32_k3"]
+    x = W.make_hidden(wl)
+    a = run_step(wl)
+    b = run_step(wl)
+    for u, v in zip(a, b):
+        np.testing.assert_array_equal(u, v)
+    # sequence 5 alone (its 4 positions) gives bitwise the same results as inside the batch
+    rows = slice(20, 24)
+    ids1, margin1, hout1 = run_step(wl, x[rows].copy(), 1, 3)
+    np.testing.assert_array_equal(ids1, a[0][rows])
+    np.testing.assert_array_equal(margin1, a[1][rows])
+    np.testing.assert_array_equal(hout1, a[2][rows])
+
+
+# ----------------------------------------------------------------------------- skewed routing
+
+
+def test_skewed_step_sampled():
+    wl = WL["skewed_b128_k3"]
+    x = W.make_hidden(wl)
+    seqs = np.random.default_rng(5).choice(wl.batch, 16, replace=False)
+    rows = tuple(int(s * (wl.drafts + 1) + j) for s in sorted(seqs) for j in range(wl.drafts + 1))
+    ref = oracle_step(wl, rows)
+    ids, margin, hout = run_step(wl)
+    dec = _check_step(wl, ref, ids, margin, hout, x, rows=rows, min_decisive=1)
+    hot = np.mean([np.isin(l["ids"], np.arange(wl.n_biased)).mean() for l in ref["layers"]])
+    log(f"  hot-expert slot fraction (sample) {hot:.3f}")
+
+
+# ----------------------------------------------------------------------------- prefill shape
+
+
+def test_prefill_sampled():
+    wl = WL["prefill_32x1156"]
+    x = W.make_hidden(wl)
+    rows = tuple(int(r) for r in np.sort(np.random.default_rng(6).choice(wl.positions, 384, replace=False)))
+    ref = oracle_step(wl, rows)
+    _, _, hout = run_step(wl)
+    dec = _check_step(wl, ref, None, None, hout, x, rows=rows, min_decisive=200)
+    m, tid, tw = run_debug_layer(wl, 0, x)
+    lay = ref["layers"][0]
+    d = lay["gap"] > GATE
+    np.testing.assert_array_equal(tid[list(rows)][d], lay["ids"][d])
+    err = row_rel_err(m[list(rows)][d], lay["m"][d])
+    log(f"  debug-layer m rel err {err:.2e} on {d.sum()} sampled rows")
+    assert err <= TOL["bf16"]
+    # the step's block output and the debug hook's agree exactly (same kernels, same order)
+    np.testing.assert_array_equal(hout, (x + m).astype(np.float32))
+
+
+def test_step_rejects_oversize():
+    wl = WL["tiny_fp32"]
+    c = context(wl)
+    T = c.cfg.max_positions + 4
+    xd = torch.zeros(T, wl.hidden, device=DEV)
+    ids = torch.empty(T, dtype=torch.int32, device=DEV)
+    with pytest.raises(bnd.MoeVerifyError) as ei:
+        c.step(xd, T, 0, ids)
+    assert ei.value.code == bnd.MOE_EINVAL
+
+
+def test_graph_replay_matches_eager():
+    """The step + acceptance captured in a HIP graph reproduce the eager results on every
+    replay, with eager work and synchronisations between replays."""
+    wl = WL["layer1_bf16"]
+    c = context(wl)
+    x = torch.from_numpy(W.make_hidden(wl)).to(DEV)
+    T, B, K = wl.positions, wl.batch, wl.drafts
+    ids = torch.empty(T, dtype=torch.int32, device=DEV)
+    margin = torch.empty(T, dtype=torch.float32, device=DEV)
+    n = torch.empty(B, dtype=torch.int32, device=DEV)
+    com = torch.empty(B, K + 1, dtype=torch.int32, device=DEV)
+    drafts = torch.zeros(B, K, dtype=torch.int32, device=DEV)
+
+    def step():
+        c.step(x, B, K, ids, margin)
+        bnd.accept_greedy(drafts, ids, B, K, n, com)
+
+    log("[graph] eager reference")
+    step()
+    torch.cuda.synchronize()
+    ref = (ids.clone(), margin.clone(), n.clone(), com.clone())
+    drafts.copy_(ids.view(B, K + 1)[:, :K])  # all drafts agree -> everything accepted
+    step()
+    torch.cuda.synchronize()
+    ref = (ids.clone(), margin.clone(), n.clone(), com.clone())
+    assert int(n[0]) == K
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    log("[graph] capture")
+    with torch.cuda.graph(g):
+        step()
+    for i in range(4):
+        ids.fill_(-1); margin.zero_(); n.fill_(-1); com.fill_(-2)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for u, v in zip((ids, margin, n, com), ref):
+            assert torch.equal(u, v), f"replay {i} differs"
+        c.step(x, B, K, ids, margin)  # eager work between replays
+        torch.cuda.synchronize()
