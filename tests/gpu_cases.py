@@ -120,6 +120,20 @@ def row_rel_err(gpu, ref):
     return float((num / np.maximum(den, 1e-30)).max()) if len(ref) else 0.0
 
 
+def end_to_end_rel_err(h_gpu, h_ref, x0, n_layers):
+    """Relative error of the summed block outputs x_L - x_0 per row, after allowing for
+    the float32 rounding of the residual adds: each of the L adds rounds x to float32 on
+    each side (<= 0.5 ulp each), so up to L ulps of |x| separate two exact-m runs; one
+    ulp of v is at most 2^-23 |v|."""
+    h_gpu = np.asarray(h_gpu, np.float64)
+    h_ref = np.asarray(h_ref, np.float64)
+    x0 = np.asarray(x0, np.float64)
+    slack = n_layers * 2.0 ** -23 * np.maximum(np.abs(h_ref).max(axis=1), np.abs(x0).max(axis=1))
+    num = np.maximum(np.abs(h_gpu - h_ref).max(axis=1) - slack, 0.0)
+    den = np.abs(h_ref - x0).max(axis=1)
+    return float((num / np.maximum(den, 1e-30)).max()) if len(x0) else 0.0
+
+
 def decisive_positions(ref):
     """Positions whose every routing gap and whose LM margin exceed GATE."""
     ok = np.ones(len(ref["hidden_out"]), bool)

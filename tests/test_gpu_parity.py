@@ -11,8 +11,8 @@ import oracle as O
 from lossless_speculative_verification_amd import binding as bnd
 from lossless_speculative_verification_amd import workload as W
 
-from gpu_cases import (DEV, GATE, TOL, context, decisive_positions, log, oracle_step, row_rel_err, run_debug_layer,
-                       run_step)
+from gpu_cases import (DEV, GATE, TOL, context, decisive_positions, end_to_end_rel_err, log, oracle_step, row_rel_err,
+                       run_debug_layer, run_step)
 
 pytestmark = pytest.mark.gpu
 
@@ -47,9 +47,7 @@ def _check_step(wl, ref, ids, margin, hout, x, rows=None, min_decisive=1):
     tol = TOL[wl.wdtype]
     dec = decisive_positions(ref)
     assert dec.sum() >= min_decisive, f"only {dec.sum()} decisive positions"
-    m_gpu = hout[sel].astype(np.float64) - x[sel]
-    m_ref = ref["hidden_out"].astype(np.float64) - x[sel]
-    err = row_rel_err(m_gpu[dec], m_ref[dec])
+    err = end_to_end_rel_err(hout[sel][dec], ref["hidden_out"][dec], x[sel][dec], wl.n_layers)
     log(f"  decisive {dec.sum()}/{len(dec)}  hidden rel err {err:.3e} (tol {tol})")
     assert err <= tol
     if wl.vocab > 0:
