@@ -80,7 +80,20 @@ def main():
     ap.add_argument("--workload", default="decode_b32_k3")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only copy 256 MiB device to device (scale reference for the HBM byte counters)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+
+        n = 256 << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "launches": 3}))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the verify step is "
               "data-parallel over sequences with no exchange, see the design notes.", file=sys.stderr)
@@ -184,6 +197,11 @@ def main():
     per_kind = {k: {"avg_us": 1000.0 * v[0] / max(v[1], 1), "launches_per_step": v[1] / args.steps}
                 for k, v in prof.items()}
     up_us = per_kind["gemm_up"]["avg_us"]
+    # measured HBM bytes per launch of the same kernel (rocprofv3 counters, see profiles/),
+    # only while the counters were taken on the current kernel sources
+    from lossless_speculative_verification_amd import profiling
+    rec = profiling.read_traffic(os.path.join(ROOT, "profiles", f"traffic_{wl.name}.md"), "k_moe_gemm<bf16,0")
+    traffic_up = rec["bytes"] if rec else None
     up_gbs = acc["up_bytes_per_launch"] / (up_us * 1e-6) / 1e9
     step_gbs = acc["step_bytes"] / (ms * 1e-3) / 1e9
 
@@ -202,9 +220,11 @@ def main():
         "config": {"workload": wl.name, "B": B, "K": K, "blocks": wl.n_layers, "hidden": wl.hidden,
                    "routed_experts": wl.n_routed, "top_k": wl.top_k, "shared_experts": wl.n_shared,
                    "inter": wl.inter, "vocab": wl.vocab, "positions": T, "mode": mode},
-        "roofline": {"bound": "hbm", "kernel": "gemm_up (gate/up + SwiGLU)", "achieved": round(up_gbs, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(up_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None},
+        "roofline": {"bound": "hbm", "kernel": "gate/up expert GEMM + SwiGLU (k_moe_gemm, one launch per block)",
+                     "achieved": round(up_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(up_gbs / HBM_PEAK_GBS, 4), "traffic": traffic_up,
+                     "algorithmic_bytes_per_launch": round(acc["up_bytes_per_launch"]),
+                     "avg_launch_us": round(up_us, 2)},
         "step_roofline": {"bound": "hbm", "achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                           "frac": round(step_gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": acc["step_bytes"],
                           "mfma_frac": round(acc["flops"] / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},

@@ -44,11 +44,16 @@ class MoeVerifyError(RuntimeError):
 _lib = None
 
 
-def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load libmoe_verify.so (once) and declare the C signatures."""
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libmoe_verify.so (once) and declare the C signatures.
+
+    The path defaults to the in-tree build, or to $MOE_VERIFY_LIB when that is set
+    (another build of the same sources, e.g. with different GEMM shape knobs).
+    """
     global _lib
     if _lib is not None:
         return _lib
+    path = path or os.environ.get("MOE_VERIFY_LIB") or LIB_PATH
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with `python -m lossless_speculative_verification_amd.build`")
     L = ctypes.CDLL(path)

@@ -25,14 +25,18 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build_library(verbose: bool = False) -> str:
-    """Compile every source into the shared library; returns its path. Always rebuilds."""
-    os.makedirs(LIB_DIR, exist_ok=True)
-    tmp = LIB_PATH + ".tmp"
+def build_library(verbose: bool = False, defines=(), out: str = LIB_PATH) -> str:
+    """Compile every source into the shared library; returns its path. Always rebuilds.
+
+    ``defines`` are extra ``NAME=VALUE`` preprocessor definitions (the streaming-GEMM
+    shape knobs in csrc/device_common.h); ``out`` is the library path to write.
+    """
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared", "-fvisibility=hidden",
            # packed-FP32 instructions stay off (see the design notes)
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+           "-I", os.path.join(ROOT, "include"), "-I", CSRC, *[f"-D{d}" for d in defines],
            *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -42,8 +46,8 @@ def build_library(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{errs}")
     if verbose and errs.strip():
         print(errs, file=sys.stderr)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

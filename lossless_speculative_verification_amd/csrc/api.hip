@@ -5,6 +5,7 @@
 // caller's stream during a step (no allocation, synchronisation or host copy there).
 #include <cstdarg>
 #include <cstdio>
+#include <algorithm>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -63,8 +64,10 @@ int check_config(const moe_verify_config* c) {
   if (c->hidden % kb || c->inter % kb)
     return fail(MOE_EUNSUPPORTED, "hidden %d and inter %d must be multiples of %d for this dtype", c->hidden,
                 c->inter, kb);
-  if (c->hidden > 4096 * (c->wdtype == MOE_BF16 ? 2 : 1) || c->inter > 16384)
-    return fail(MOE_EUNSUPPORTED, "hidden %d or inter %d too large", c->hidden, c->inter);
+  // hidden: one residual row is held in 16 float4 per lane; the router's LDS rows fit 64 KB
+  if (c->hidden > (c->wdtype == MOE_BF16 ? 4096 : 2048) || c->inter > 16384)
+    return fail(MOE_EUNSUPPORTED, "hidden %d (max %d for this dtype) or inter %d (max 16384) too large", c->hidden,
+                c->wdtype == MOE_BF16 ? 4096 : 2048, c->inter);
   if (max_work_items(*c, c->max_positions) > 65535 || (int64_t)c->max_positions * c->top_k > (1ll << 30))
     return fail(MOE_EUNSUPPORTED, "max_positions %d too large", c->max_positions);
   return MOE_OK;
@@ -104,6 +107,7 @@ struct DeviceGuard {
 struct moe_verify_ctx {
   moe_verify_config cfg{};
   int device = 0;
+  int n_cu = 256;  // compute units of the device (sizes the streaming GEMM grids)
   int es = 2;
   int NQ_up = 0, NQ_dn = 0, NQ_lm = 0, n_pg_lm = 0, NKB_H = 0, NKB_I = 0;
   size_t router_units_per_layer = 0, up_units_per_layer = 0, down_units_per_layer = 0;
@@ -175,16 +179,25 @@ namespace {
 int run_block(moe_verify_ctx* c, int l, const float* x_in, const float* ybuf_prev, int Tn, hipStream_t st) {
   const moe_verify_config& g = c->cfg;
   const int E = g.n_routed, S = g.n_shared, k = g.top_k, KS = k + S, H = g.hidden, I = g.inter;
+  const int wmax = (int)max_work_items(g, Tn);
+  mv::PlanArgs pa{};
+  pa.topk_id = c->topk_id;
+  pa.topk_w = c->topk_w;
+  pa.Tn = Tn; pa.k = k; pa.E = E; pa.S = S;
+  pa.row_tok = c->row_tok;
+  pa.row_dst = c->row_dst;
+  pa.row_gate = c->row_gate;
+  pa.work = c->work;
+  pa.n_work = c->n_work;
+  pa.counts = c->counts + (size_t)l * E;
   c->prof_begin(MOE_PROF_NORM_ROUTE, st);
   MV_CHECK(mv::launch_norm_route(g.wdtype, true, x_in, ybuf_prev, c->x_ws, nullptr, c->a,
                                  c->router_p + l * c->router_units_per_layer, c->bias_p + (size_t)l * 64, c->topk_id,
                                  c->topk_w, Tn, H, KS, E, k, g.rms_eps, st));
   c->prof_end(st);
   c->prof_begin(MOE_PROF_PLAN, st);
-  MV_CHECK(mv::launch_plan(c->topk_id, c->topk_w, Tn, k, E, S, c->row_tok, c->row_dst, c->row_gate, c->work,
-                           c->n_work, c->counts + (size_t)l * E, st));
+  MV_CHECK(mv::launch_plan(pa, st));
   c->prof_end(st);
-  const int wmax = (int)max_work_items(g, Tn);
   mv::GemmArgs a{};
   a.work = c->work;
   a.n_work = c->n_work;
@@ -193,6 +206,16 @@ int run_block(moe_verify_ctx* c, int l, const float* x_in, const float* ybuf_pre
   a.row_tok = c->row_tok;
   a.row_dst = c->row_dst;
   a.row_gate = c->row_gate;
+  a.max_items = wmax;
+  // Two pairs per wavefront when the expected items x pairs fill at least one round of
+  // resident wavefronts (routed items: one per touched expert while positions are few).
+  const int wave_target = c->n_cu * mv::kGemmWaves * MV_GEMM_WAVES_PER_SIMD;
+  const int mb = mv::kGemmMB;
+  const int est_items = std::min(E, Tn * k) + S * ((Tn + mb - 1) / mb);
+  auto chunks_for = [&](int NQ, int* ppw) {
+    *ppw = est_items * NQ >= wave_target ? 2 : 1;
+    return (NQ + *ppw - 1) / *ppw;
+  };
   // gate/up + SwiGLU
   a.A = c->a;
   a.B = c->up_p + l * c->up_units_per_layer;
@@ -200,7 +223,8 @@ int run_block(moe_verify_ctx* c, int l, const float* x_in, const float* ybuf_pre
   a.NQ = c->NQ_up;
   a.h = c->h;
   c->prof_begin(MOE_PROF_GEMM_UP, st);
-  MV_CHECK(mv::launch_gemm(g.wdtype, mv::EPI_UP, a, dim3((c->NQ_up + mv::kGemmWaves - 1) / mv::kGemmWaves, wmax), st));
+  int ch = chunks_for(c->NQ_up, &a.ppw);
+  MV_CHECK(mv::launch_gemm(g.wdtype, mv::EPI_UP, a, (unsigned)((wmax * ch + mv::kGemmWaves - 1) / mv::kGemmWaves), st));
   c->prof_end(st);
   // down + gate scale
   a.A = c->h;
@@ -209,7 +233,8 @@ int run_block(moe_verify_ctx* c, int l, const float* x_in, const float* ybuf_pre
   a.NQ = c->NQ_dn;
   a.ybuf = c->ybuf;
   c->prof_begin(MOE_PROF_GEMM_DOWN, st);
-  MV_CHECK(mv::launch_gemm(g.wdtype, mv::EPI_DOWN, a, dim3((c->NQ_dn + mv::kGemmWaves - 1) / mv::kGemmWaves, wmax), st));
+  ch = chunks_for(c->NQ_dn, &a.ppw);
+  MV_CHECK(mv::launch_gemm(g.wdtype, mv::EPI_DOWN, a, (unsigned)((wmax * ch + mv::kGemmWaves - 1) / mv::kGemmWaves), st));
   c->prof_end(st);
   return MOE_OK;
 }
@@ -251,10 +276,12 @@ MV_API int moe_verify_init(const moe_verify_config* cfg, const moe_verify_weight
   c->cfg = g;
   c->es = elem_bytes(g.wdtype);
   hipError_t he = hipGetDevice(&c->device);
+  if (he == hipSuccess) he = hipDeviceGetAttribute(&c->n_cu, hipDeviceAttributeMultiprocessorCount, c->device);
   if (he != hipSuccess) {
     delete c;
-    return fail(MOE_EDEVICE, "hipGetDevice: %s", hipGetErrorString(he));
+    return fail(MOE_EDEVICE, "device query: %s", hipGetErrorString(he));
   }
+  if (c->n_cu < 1) c->n_cu = 1;
   const int E = g.n_routed, S = g.n_shared, k = g.top_k, KS = k + S, H = g.hidden, I = g.inter, L = g.n_layers;
   const size_t es = c->es, P = (size_t)g.max_positions;
   c->NKB_H = (int)(H * es / mv::kRowBlockBytes);
@@ -346,6 +373,13 @@ MV_API int moe_verify_step(moe_verify_ctx* c, const float* hidden_in, int32_t B,
                                  nullptr, nullptr, Tn, g.hidden, KS, g.n_routed, g.top_k, g.rms_eps, st));
   c->prof_end(st);
   if (g.vocab > 0) {
+    // Workgroups (4 wavefronts, two per CU) cover one row block of up to kLmRows
+    // positions; pairs per wavefront so that the workgroups of one row block make about
+    // one round on the device (further row blocks share the weight stream through L2).
+    const int n_items = (Tn + mv::kLmRows - 1) / mv::kLmRows;
+    const int target = c->n_cu * mv::kGemmWaves * 2;  // pair streams per round
+    const int ppw = std::max(1, (c->NQ_lm + target - 1) / target);
+    const int n_pg = (c->NQ_lm + mv::kGemmWaves * ppw - 1) / (mv::kGemmWaves * ppw);
     mv::GemmArgs a{};
     a.A = c->a;
     a.B = c->lm_p;
@@ -354,12 +388,13 @@ MV_API int moe_verify_step(moe_verify_ctx* c, const float* hidden_in, int32_t B,
     a.n_valid = g.vocab;
     a.Tn = Tn;
     a.part = c->part;
-    a.n_pg = c->n_pg_lm;
+    a.n_pg = n_pg;
+    a.lm_ppw = ppw;
     c->prof_begin(MOE_PROF_LM_HEAD, st);
-    MV_CHECK(mv::launch_gemm(g.wdtype, mv::EPI_LM, a, dim3(c->n_pg_lm, (Tn + mv::kGemmMB - 1) / mv::kGemmMB), st));
+    MV_CHECK(mv::launch_gemm(g.wdtype, mv::EPI_LM, a, (unsigned)(n_items * n_pg), st));
     c->prof_end(st);
     c->prof_begin(MOE_PROF_ARGMAX, st);
-    MV_CHECK(mv::launch_argmax_reduce(c->part, c->n_pg_lm, Tn, argmax_out, margin_out, st));
+    MV_CHECK(mv::launch_argmax_reduce(c->part, n_pg, Tn, argmax_out, margin_out, st));
     c->prof_end(st);
   }
   return ok();

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace mv {
 
 constexpr int kWave = 64;           // CDNA wavefront width
@@ -11,11 +13,34 @@ constexpr int kRowBlockBytes = 256; // bytes of one row per K block of the packe
 constexpr int kChunksPerRow = kRowBlockBytes / 16;  // 16-byte chunks per row per K block
 constexpr int kPairUnits = 2 * 4 * kWave;           // 16-byte units per (pair, K block) = 8 KB
 constexpr int kGemmWaves = 4;                       // waves per GEMM workgroup (one pair each)
-constexpr int kGemmMB = 64;                         // rows per GEMM work item (max M per pass)
+// Streaming GEMM shape: row tiles (16 rows each) per work item and K blocks in flight
+// per wavefront, for the expert GEMMs and the LM head.
+#ifndef MV_GEMM_NMT
+#define MV_GEMM_NMT 2
+#endif
+#ifndef MV_GEMM_D
+#define MV_GEMM_D 2
+#endif
+#ifndef MV_GEMM_WAVES_PER_SIMD
+#define MV_GEMM_WAVES_PER_SIMD 2
+#endif
+constexpr int kGemmMB = 16 * MV_GEMM_NMT;           // rows per expert GEMM work item
+constexpr int kLmRows = 128;                        // positions per LM-head row block
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// Calls f(std::integral_constant<int, i>{}) for i = 0..N-1: a loop whose index must be a
+// compile-time constant (it selects a register array of a software pipeline).
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 // bf16 is carried as uint16_t bit patterns.
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }

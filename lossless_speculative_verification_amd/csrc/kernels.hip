@@ -81,154 +81,225 @@ __global__ void k_repack_router(const uint8_t* __restrict__ src, uint4* __restri
 
 // ============================================================================ norm + router + top-k
 
-// One wavefront per position, four per workgroup.
-//  1. x = x_in + sum_j ybuf[j] (j = 0..KS-1 in order; absent for the first block);
-//     x is written back as the residual stream (and to x_copy when given).
-//  2. a = x / sqrt(mean(x^2) + eps), stored in the element type (bf16 rounding).
-//  3. (route) logits r_e = a . W_r[e] + bias_e, lane e = expert e (E <= 64), float32.
-//  4. (route) k rounds of a wavefront argmax (larger logit, then lower index) give the
-//     selected experts in slot order; gates = softmax of the selected logits.
-template <typename T, bool ROUTE>
+// Four consecutive elements (one float4 of the residual row) stored as the element type.
+__device__ __forceinline__ void store4(float* p, size_t i4, float4 u) { reinterpret_cast<float4*>(p)[i4] = u; }
+__device__ __forceinline__ void store4(uint16_t* p, size_t i4, float4 u) {
+  uint2 w;
+  w.x = f32_to_bf16(u.x) | (f32_to_bf16(u.y) << 16);
+  w.y = f32_to_bf16(u.z) | (f32_to_bf16(u.w) << 16);
+  reinterpret_cast<uint2*>(p)[i4] = w;
+}
+
+// One workgroup of four wavefronts handles NP consecutive positions; VM float4 per lane
+// hold one residual row (H <= 256 * VM).
+//  1. (wavefront per position) x = x_in + (y_0 + ... + y_{KS-1}) with the previous
+//     block's per-slot outputs summed in slot order (absent for the first block); x is
+//     written back as the residual stream (and to x_copy when given). The slot rows are
+//     read SB at a time with all their loads in flight together.
+//  2. a = x / sqrt(mean(x^2) + eps), stored in the element type (bf16 rounding) to a_out
+//     and, for routing, to LDS.
+//  3. (route) router logits for the NP positions as a small MFMA product: wavefront w
+//     computes experts 16w..16w+15 against all NP rows (the 16-row MFMA tile repeats
+//     row 0 in its unused rows, whose results are dropped), float32 accumulation. The
+//     first half of the router weights is requested before step 1, so its latency
+//     overlaps the residual reads.
+//  4. (route, wavefront per position) logit of expert e in lane e plus its bias; k
+//     rounds of a wavefront argmax (larger logit, then lower index) give the selected
+//     experts in slot order; the gates are the softmax of the selected logits.
+// Loads never sit behind a branch (the compiler would then wait for every load in
+// flight at the join): indices past the end are clamped and their values masked.
+template <typename T, bool ROUTE, int NP, int VM>
 __global__ __launch_bounds__(256) void k_norm_route(const float* x_in, const float* __restrict__ ybuf,
                                                     float* x_out, float* __restrict__ x_copy,
                                                     T* __restrict__ a_out, const uint4* __restrict__ wr,
                                                     const float* __restrict__ bias,
                                                     int32_t* __restrict__ topk_id, float* __restrict__ topk_w,
                                                     int Tn, int H, int KS, int E, int k, float eps) {
-  extern __shared__ uint4 a_lds_raw[];
+  constexpr int SB = VM <= 5 ? 8 : 4;  // slot rows read together
+  constexpr int RB = 20;               // router K chunks (64 bytes of a row each) per load batch
+  extern __shared__ uint4 lds_raw[];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + wave;
-  const bool valid = t < Tn;  // every wavefront stays to the workgroup barrier below
   const int H4 = H >> 2;
-  const size_t t0 = valid ? (size_t)t : 0;
-  const float4* xi = reinterpret_cast<const float4*>(x_in) + t0 * H4;
-  float4* xo = x_out ? reinterpret_cast<float4*>(x_out) + t0 * H4 : nullptr;
-  float4* xc = x_copy ? reinterpret_cast<float4*>(x_copy) + t0 * H4 : nullptr;
-  const float4* yb0 = ybuf ? reinterpret_cast<const float4*>(ybuf) + t0 * KS * H4 : nullptr;
+  const int row_stride = H * (int)sizeof(T) + 16;  // bytes; the pad spreads rows over banks
+  char* a_lds = reinterpret_cast<char*>(lds_raw);
+  float* r_lds = reinterpret_cast<float*>(a_lds + (size_t)NP * row_stride);
 
-  // x = x_in + (y_0 + y_1 + ... + y_{KS-1}), the block output summed in slot order.
-  auto residual = [&](int i) {
-    float4 v = xi[i];
-    if (yb0) {
-      float4 m = yb0[i];
-      for (int j = 1; j < KS; ++j) {
-        const float4 y = yb0[(size_t)j * H4 + i];
-        m.x += y.x; m.y += y.y; m.z += y.z; m.w += y.w;
-      }
-      v.x += m.x; v.y += m.y; v.z += m.z; v.w += m.w;
-    }
-    return v;
-  };
-
-  float ss = 0.f;
-  if (valid) {
-    for (int i = lane; i < H4; i += kWave) {
-      const float4 v = residual(i);
-      if (xo) xo[i] = v;
-      if (xc) xc[i] = v;
-      ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-    }
-  }
-  ss = wave_sum(ss);
-  const float inv = 1.0f / sqrtf(ss / (float)H + eps);
-
-  // Normalise. x is re-read from what this lane itself wrote (x_out), or recomputed
-  // the same way when there is no x_out; each lane touches only its own elements.
-  T* a_lds = reinterpret_cast<T*>(a_lds_raw) + (size_t)wave * H;
-  T* arow = a_out + t0 * H;
-  if (valid) {
-    for (int i = lane; i < H4; i += kWave) {
-      const float4 v = xo ? xo[i] : residual(i);
-      const float u[4] = {v.x * inv, v.y * inv, v.z * inv, v.w * inv};
+  const int e0 = wave * 16;
+  const bool route_wave = ROUTE && e0 < E;
+  const int n64 = H * (int)sizeof(T) / 64;
+  const uint4* wp = wr + (size_t)(lane >> 4) * kWave + e0 + (lane & 15);
+  uint4 wbuf[RB];
+  if (route_wave) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        store_elem(arow, (size_t)4 * i + c, u[c]);
-        if (ROUTE) store_elem(a_lds, (size_t)4 * i + c, u[c]);
+    for (int i = 0; i < RB; ++i) wbuf[i] = wp[(size_t)min(i, n64 - 1) * 4 * kWave];
+  }
+
+#pragma unroll 1
+  for (int p = wave; p < NP; p += kGemmWaves) {
+    const int t = blockIdx.x * NP + p;
+    if (t >= Tn) continue;
+    const float4* xi = reinterpret_cast<const float4*>(x_in) + (size_t)t * H4;
+    float4 v[VM];
+    if (ybuf) {
+      const float4* yb = reinterpret_cast<const float4*>(ybuf) + (size_t)t * KS * H4;
+      float4 m[VM];
+#pragma unroll
+      for (int j = 0; j < VM; ++j) m[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int s0 = 0; s0 < KS; s0 += SB) {
+        float4 y[SB][VM];
+#pragma unroll
+        for (int s = 0; s < SB; ++s)
+#pragma unroll
+          for (int j = 0; j < VM; ++j)
+            y[s][j] = yb[(size_t)min(s0 + s, KS - 1) * H4 + min(lane + kWave * j, H4 - 1)];
+#pragma unroll
+        for (int s = 0; s < SB; ++s)
+#pragma unroll
+          for (int j = 0; j < VM; ++j) {
+            const bool ok = s0 + s < KS && lane + kWave * j < H4;
+            m[j].x += ok ? y[s][j].x : 0.f;
+            m[j].y += ok ? y[s][j].y : 0.f;
+            m[j].z += ok ? y[s][j].z : 0.f;
+            m[j].w += ok ? y[s][j].w : 0.f;
+          }
+      }
+#pragma unroll
+      for (int j = 0; j < VM; ++j) {
+        const float4 x = xi[min(lane + kWave * j, H4 - 1)];
+        v[j] = make_float4(x.x + m[j].x, x.y + m[j].y, x.z + m[j].z, x.w + m[j].w);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < VM; ++j) v[j] = xi[min(lane + kWave * j, H4 - 1)];
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < VM; ++j) {
+      const int i = lane + kWave * j;
+      if (i < H4) {
+        if (x_out) reinterpret_cast<float4*>(x_out)[(size_t)t * H4 + i] = v[j];
+        if (x_copy) reinterpret_cast<float4*>(x_copy)[(size_t)t * H4 + i] = v[j];
+        ss += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
+      }
+    }
+    ss = wave_sum(ss);
+    const float inv = 1.0f / sqrtf(ss / (float)H + eps);
+    T* lrow = reinterpret_cast<T*>(a_lds + (size_t)p * row_stride);
+#pragma unroll
+    for (int j = 0; j < VM; ++j) {
+      const int i = lane + kWave * j;
+      if (i < H4) {
+        const float4 u = make_float4(v[j].x * inv, v[j].y * inv, v[j].z * inv, v[j].w * inv);
+        store4(a_out + (size_t)t * H, i, u);
+        if (ROUTE) store4(lrow, i, u);
       }
     }
   }
   if (!ROUTE) return;
   __syncthreads();
-  if (!valid) return;
 
-  // Router logits: lane e accumulates a . W_r[e] over the row in order.
-  constexpr int P = Elem<T>::per16;
-  const int chunks = H / P;
-  const uint4* al = reinterpret_cast<const uint4*>(a_lds);
-  float acc = 0.f;
-#pragma unroll 8
-  for (int c = 0; c < chunks; ++c) {
-    const uint4 w = wr[(size_t)c * 64 + lane];
-    const uint4 av = al[c];
-    const T* wp = reinterpret_cast<const T*>(&w);
-    const T* ap = reinterpret_cast<const T*>(&av);
+  // Router logits r[p][e] = a_p . W_r[e] for this workgroup's positions.
+  if (route_wave) {
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    const int row = (lane & 15) < NP ? (lane & 15) : 0;
+    const uint4* arow = reinterpret_cast<const uint4*>(a_lds + (size_t)row * row_stride) + (lane >> 4);
+    const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+    for (int c0 = 0; c0 < n64; c0 += RB) {
+      if (c0 > 0) {
 #pragma unroll
-    for (int i = 0; i < P; ++i) acc += Elem<T>::load(ap, i) * Elem<T>::load(wp, i);
-  }
-  const float NEG = -__builtin_huge_valf();
-  float r = lane < E ? acc + bias[lane] : NEG;
-  if (r != r) r = NEG;  // a NaN logit ranks last, so every selected id stays below E
-
-  // Top-k by repeated wavefront argmax; lane j keeps the j-th selection.
-  bool taken = false;
-  float my_v = NEG, v0 = 0.f;
-  int my_e = 0;
-  for (int j = 0; j < k; ++j) {
-    float bv = taken ? NEG : r;
-    int bi = taken ? INT_MAX : lane;
+        for (int i = 0; i < RB; ++i) wbuf[i] = wp[(size_t)min(c0 + i, n64 - 1) * 4 * kWave];
+      }
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-      const float ov = __shfl_xor(bv, m, kWave);
-      const int oi = __shfl_xor(bi, m, kWave);
-      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+      for (int i = 0; i < RB; ++i) {
+        const bool ok = c0 + i < n64;  // a zero weight chunk adds exactly nothing
+        mma_chunk(acc, arow[min(c0 + i, n64 - 1) * 4], ok ? wbuf[i] : zero, (T*)nullptr);
+      }
     }
-    if (lane == bi) taken = true;
-    if (lane == j) { my_v = bv; my_e = bi; }
-    if (j == 0) v0 = bv;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int p = 4 * (lane >> 4) + i;
+      if (p < NP) r_lds[p * 64 + e0 + (lane & 15)] = acc[i];
+    }
   }
-  const float z = lane < k ? expf(my_v - v0) : 0.f;
-  const float Z = wave_sum(z);
-  if (lane < k) {
-    topk_id[(size_t)t * k + lane] = my_e;
-    topk_w[(size_t)t * k + lane] = z / Z;
+  __syncthreads();
+
+  const float NEG = -__builtin_huge_valf();
+#pragma unroll 1
+  for (int p = wave; p < NP; p += kGemmWaves) {
+    const int t = blockIdx.x * NP + p;
+    if (t >= Tn) continue;
+    float r = lane < E ? r_lds[p * 64 + lane] + bias[lane] : NEG;
+    if (r != r) r = NEG;  // a NaN logit ranks last, so every selected id stays below E
+    // Top-k by repeated wavefront argmax; lane j keeps the j-th selection.
+    bool taken = false;
+    float my_v = NEG, v0 = 0.f;
+    int my_e = 0;
+    for (int j = 0; j < k; ++j) {
+      float bv = taken ? NEG : r;
+      int bi = taken ? INT_MAX : lane;
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) {
+        const float ov = __shfl_xor(bv, m, kWave);
+        const int oi = __shfl_xor(bi, m, kWave);
+        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+      }
+      if (lane == bi) taken = true;
+      if (lane == j) { my_v = bv; my_e = bi; }
+      if (j == 0) v0 = bv;
+    }
+    const float z = lane < k ? expf(my_v - v0) : 0.f;
+    const float Z = wave_sum(z);
+    if (lane < k) {
+      topk_id[(size_t)t * k + lane] = my_e;
+      topk_w[(size_t)t * k + lane] = z / Z;
+    }
   }
+
 }
 
 // ============================================================================ routing plan
 
-// One workgroup of 16 wavefronts orders the T*k routed slots (slot = t*k + j) by
-// expert, stably (ascending slot within an expert), and lists the GEMM work items.
-//  phase 1: per-wavefront expert histograms of 16 contiguous slot segments;
+// The routing plan, computed by one workgroup of NW wavefronts: it orders the T*k routed
+// slots (slot = t*k + j) by expert, stably (ascending slot within an expert), and lists
+// the GEMM work items.
+//  phase 1: per-wavefront expert histograms of NW contiguous slot segments;
 //  phase 2: exclusive scan in (expert, segment) order -> each segment's write base;
 //  phase 3: each wavefront places its segment 64 slots at a time; lanes with the same
 //           expert are found with six ballots over the expert id bits, and a lane's
 //           rank is the count of lower lanes in its group;
-//  phase 4: work items of at most kGemmMB rows: routed experts first (expert order),
-//           then each shared expert's position blocks.
+//  phase 4: work items of at most kGemmMB rows: each shared expert's position blocks
+//           first (so the blocks of one shared expert are neighbours in the item list),
+//           then the routed experts' row blocks in expert order.
 // Routed rows occupy [0, T*k) of the row space; shared expert s owns rows
 // T*k + s*T + t.
-__global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ topk_id,
-                                               const float* __restrict__ topk_w, int Tn, int k, int E, int S,
-                                               int32_t* __restrict__ row_tok, int32_t* __restrict__ row_dst,
-                                               float* __restrict__ row_gate, int4* __restrict__ work,
-                                               int32_t* __restrict__ n_work, int32_t* __restrict__ counts) {
-  __shared__ int hist[16][64];
-  __shared__ int off[65];
-  __shared__ int wstart[65];
+
+template <int NW>
+__device__ void plan_body(const PlanArgs& pa, int (*hist)[64], int* off, int* wstart) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int E = pa.E, S = pa.S, k = pa.k, Tn = pa.Tn;
   const int N = Tn * k, KS = k + S;
   hist[wave][lane] = 0;
   __syncthreads();
 
-  const int seg = (N + 15) / 16;
+  // Each wavefront reads its segment PB*64 slots at a time, all loads of a batch in
+  // flight together (one memory round trip per batch rather than per 64 slots).
+  constexpr int PB = 8;
+  const int seg = (N + NW - 1) / NW;
   const int beg = min(N, wave * seg), end = min(N, beg + seg);
-  for (int i = beg + lane; i < end; i += kWave) atomicAdd(&hist[wave][min(max(topk_id[i], 0), E - 1)], 1);
+  for (int b0 = beg; b0 < end; b0 += PB * kWave) {
+    int key[PB];
+#pragma unroll
+    for (int u = 0; u < PB; ++u) key[u] = pa.topk_id[min(b0 + u * kWave + lane, N - 1)];
+#pragma unroll
+    for (int u = 0; u < PB; ++u)
+      if (b0 + u * kWave + lane < end) atomicAdd(&hist[wave][min(max(key[u], 0), E - 1)], 1);
+  }
   __syncthreads();
 
   if (wave == 0) {
     int c = 0;
     if (lane < E)
-      for (int w = 0; w < 16; ++w) c += hist[w][lane];
+      for (int w = 0; w < NW; ++w) c += hist[w][lane];
     const int nb = (c + kGemmMB - 1) / kGemmMB;
     // inclusive scans over lanes of c and nb
     int sc = c, sn = nb;
@@ -239,10 +310,10 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ topk_
     }
     off[lane] = sc - c;
     wstart[lane] = sn - nb;
-    if (lane < E) counts[lane] = c;
+    if (lane < E) pa.counts[lane] = c;
     if (lane == 63) { off[64] = sc; wstart[64] = sn; }
     int run = sc - c;
-    for (int w = 0; w < 16; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const int h = hist[w][lane];
       hist[w][lane] = run;  // becomes the segment's write cursor for this expert
       run += h;
@@ -250,224 +321,436 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ topk_
   }
   __syncthreads();
 
-  for (int b0 = beg; b0 < end; b0 += kWave) {
-    const int i = b0 + lane;
-    const bool active = i < end;
-    const int key = active ? min(max(topk_id[i], 0), E - 1) : 0;  // ids come from k_norm_route, always < E
-    unsigned long long mask = __ballot(active);
+  for (int b0 = beg; b0 < end; b0 += PB * kWave) {
+    int keys[PB];
+    float gates[PB];
 #pragma unroll
-    for (int bit = 0; bit < 6; ++bit) {
-      const bool on = (key >> bit) & 1;
-      const unsigned long long bal = __ballot(on);
-      mask &= on ? bal : ~bal;
+    for (int u = 0; u < PB; ++u) {
+      const int i = min(b0 + u * kWave + lane, N - 1);
+      keys[u] = pa.topk_id[i];
+      gates[u] = pa.topk_w[i];
     }
-    const int rank = __popcll(mask & ((1ull << lane) - 1ull));
-    const int cnt = __popcll(mask);
-    int pos = 0;
-    if (active) pos = hist[wave][key] + rank;
-    __builtin_amdgcn_wave_barrier();
-    if (active) {
-      const int tok = i / k, j = i - tok * k;
-      row_tok[pos] = tok;
-      row_dst[pos] = tok * KS + j;
-      row_gate[pos] = topk_w[i];
-      if (rank == cnt - 1) hist[wave][key] = pos + 1;
+#pragma unroll
+    for (int u = 0; u < PB; ++u) {
+      const int i = b0 + u * kWave + lane;
+      if (b0 + u * kWave >= end) break;  // wavefront-uniform
+      const bool active = i < end;
+      const int key = active ? min(max(keys[u], 0), E - 1) : 0;  // ids come from k_norm_route, always < E
+      unsigned long long mask = __ballot(active);
+#pragma unroll
+      for (int bit = 0; bit < 6; ++bit) {
+        const bool on = (key >> bit) & 1;
+        const unsigned long long bal = __ballot(on);
+        mask &= on ? bal : ~bal;
+      }
+      const int rank = __popcll(mask & ((1ull << lane) - 1ull));
+      const int cnt = __popcll(mask);
+      int pos = 0;
+      if (active) pos = hist[wave][key] + rank;
+      __builtin_amdgcn_wave_barrier();
+      if (active) {
+        const int tok = i / k, j = i - tok * k;
+        pa.row_tok[pos] = tok;
+        pa.row_dst[pos] = tok * KS + j;
+        pa.row_gate[pos] = gates[u];
+        if (rank == cnt - 1) hist[wave][key] = pos + 1;
+      }
+      __builtin_amdgcn_wave_barrier();
     }
-    __builtin_amdgcn_wave_barrier();
   }
 
+  const int mbT = (Tn + kGemmMB - 1) / kGemmMB;
+  const int nsw = S * mbT;  // shared-expert items come first
+  for (int idx = tid; idx < nsw; idx += NW * kWave) {
+    const int s = idx / mbT, b = idx - s * mbT;
+    pa.work[idx] = make_int4(E + s, N + s * Tn + b * kGemmMB, min(kGemmMB, Tn - b * kGemmMB), b * kGemmMB);
+  }
   if (tid < E) {
     const int c = off[tid + 1] - off[tid];
     for (int b = 0; b * kGemmMB < c; ++b)
-      work[wstart[tid] + b] = make_int4(tid, off[tid] + b * kGemmMB, min(kGemmMB, c - b * kGemmMB), 0);
+      pa.work[nsw + wstart[tid] + b] = make_int4(tid, off[tid] + b * kGemmMB, min(kGemmMB, c - b * kGemmMB), 0);
   }
-  const int nrw = wstart[64];
-  const int mbT = (Tn + kGemmMB - 1) / kGemmMB;
-  for (int idx = tid; idx < S * mbT; idx += 1024) {
-    const int s = idx / mbT, b = idx - s * mbT;
-    work[nrw + idx] = make_int4(E + s, N + s * Tn + b * kGemmMB, min(kGemmMB, Tn - b * kGemmMB), b * kGemmMB);
-  }
-  if (tid == 0) *n_work = nrw + S * mbT;
+  if (tid == 0) *pa.n_work = nsw + wstart[64];
+}
+
+__global__ __launch_bounds__(1024) void k_plan(PlanArgs pa) {
+  __shared__ int hist[16][64];
+  __shared__ int off[65];
+  __shared__ int wstart[65];
+  plan_body<16>(pa, hist, off, wstart);
 }
 
 // ============================================================================ grouped MFMA GEMM
 
-// One workgroup = 4 wavefronts = 4 column pairs (2 x 16 output columns each) of one
-// expert, for up to kGemmMB rows of that expert (one work item). Weights stream from
-// HBM once, straight into registers, in the pair layout (8 coalesced 1 KB loads per
-// wavefront per 256-byte K block, two K blocks in flight). The work item's activation
-// rows are staged in LDS one K block at a time (double-buffered, one 16-byte pad per
-// row so the 16 rows an MFMA reads hit distinct banks) and read as MFMA A operands.
-// Products accumulate in float32 MFMA (16x16x32 bf16 or 16x16x4 f32).
+// Logical workgroup index of hardware workgroup h when the first n carry work.
+// Workgroups are dealt to the 8 XCDs round-robin; here each XCD takes one contiguous
+// range of logical indices instead, so logical neighbours (the row blocks of one expert,
+// which stream the same weights) share one L2.
+__device__ __forceinline__ int xcd_logical(int h, int n) {
+  const int x = h & 7, j = h >> 3;
+  int start = 0;
+  for (int y = 0; y < x; ++y) start += (n - y + 7) >> 3;
+  return start + j;
+}
+
+// One wavefront computes PPW consecutive column pairs (2 x 16 output columns each) of one
+// expert work item (up to 16*NMT rows) over the whole contraction, the pairs side by
+// side so that one loop serves them all:
+//  * weights stream from HBM once, in the pair layout: per 256-byte K block and pair,
+//    8 fully coalesced 1 KB non-temporal loads; D K blocks in flight;
+//  * the item's activation rows are read straight from global memory (small and
+//    L2-resident), once per K block for all PPW pairs: lane l reads row 16*mt + l%16
+//    of each row tile, the 64 bytes of the K block that its lane group l/16 contracts;
+//    rows past the item's end repeat row 0 and their results are dropped;
+//  * products accumulate in float32 MFMA (16x16x32 bf16, or 16x16x4 f32).
+// The main loop holds only loads and MFMAs, and no load in it depends on a branch: a
+// store, a spill or a conditional load there would make the compiler wait for every
+// load in flight. The epilogue follows the loop:
 //   UP:   tile t = 0 is the gate projection, t = 1 the up projection of the same 16
 //         intermediate columns; the epilogue forms silu(gate) * up and stores it.
 //   DOWN: the epilogue scales by the row's gate (1 for shared experts) and writes the
-//         row's own ybuf slot; no two workgroups write the same element.
-//   LM:   the epilogue reduces each row's 32 logits per wavefront to (top-1 value,
-//         lowest index, top-2 value), then across the 4 wavefronts; one record per row
-//         and workgroup goes to `part`.
-template <typename T, int EPI>
-__global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
-  constexpr int MT = kGemmMB / 16;
-  __shared__ uint4 As[2][kGemmMB][kChunksPerRow + 1];
-  __shared__ Top2 red[EPI == EPI_LM ? kGemmWaves : 1][EPI == EPI_LM ? kGemmMB : 1];
-
-  const int pg = blockIdx.x;
-  int e, row0, M, tok0;
-  if (EPI == EPI_LM) {
-    e = 0;
-    row0 = blockIdx.y * kGemmMB;
-    M = min(kGemmMB, g.Tn - row0);
-    tok0 = row0;
-    if (M <= 0) return;
-  } else {
-    if ((int)blockIdx.y >= *g.n_work) return;
-    const int4 it = g.work[blockIdx.y];
-    e = it.x; row0 = it.y; M = it.z; tok0 = it.w;
-  }
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int q = pg * kGemmWaves + wave;
-  const bool qok = q < g.NQ;
+//         row's own ybuf slot; no two wavefronts write the same element.
+// There is no LDS and no barrier: wavefronts run free.
+template <typename T, int EPI, int NMT, int PPW, int D>
+__device__ __forceinline__ void moe_stream(const GemmArgs& g, int e, int row0, int M, int tok0, int q0) {
+  const int lane = threadIdx.x & 63;
   const int row_units = g.K * (int)sizeof(T) / 16;
   const int NKB = row_units / kChunksPerRow;
-  const uint4* Bq = g.B + ((size_t)e * g.NQ + (qok ? q : 0)) * (size_t)NKB * kPairUnits + lane;
-
-  // Activation staging: thread -> row srow + 16*it, 16-byte chunk schunk of the K block.
-  const int srow = threadIdx.x >> 4, schunk = threadIdx.x & 15;
-  const uint4* arow[MT];
-#pragma unroll
-  for (int it = 0; it < MT; ++it) {
-    const int r = srow + 16 * it;
-    arow[it] = nullptr;
-    if (r < M) {
-      int src;
-      if (EPI == EPI_UP) src = (e < g.E) ? g.row_tok[row0 + r] : tok0 + r;
-      else if (EPI == EPI_DOWN) src = row0 + r;
-      else src = tok0 + r;
-      arow[it] = reinterpret_cast<const uint4*>(g.A) + (size_t)src * row_units + schunk;
-    }
-  }
-  uint4 ra[MT], rb0[8], rb1[8];
-  auto load_a = [&](int kb) {
-#pragma unroll
-    for (int it = 0; it < MT; ++it) ra[it] = arow[it] ? arow[it][kb * kChunksPerRow] : make_uint4(0u, 0u, 0u, 0u);
-  };
-  auto store_a = [&](int buf) {
-#pragma unroll
-    for (int it = 0; it < MT; ++it) As[buf][srow + 16 * it][schunk] = ra[it];
-  };
-  auto load_b = [&](int kb, uint4(&rb)[8]) {
-    if (!qok) return;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) rb[u] = load_stream(Bq + (size_t)kb * kPairUnits + u * kWave);
-  };
-
-  f32x4_t acc[MT][2];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt][0] = acc[mt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const int n_mt = (M + 15) >> 4;
-  auto compute = [&](int buf, const uint4(&rb)[8]) {
-    if (!qok) return;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        if (mt < n_mt) {
-          const uint4 a = As[buf][mt * 16 + (lane & 15)][(lane >> 4) * 4 + s];
-          mma_chunk(acc[mt][0], a, rb[s], (T*)nullptr);
-          mma_chunk(acc[mt][1], a, rb[4 + s], (T*)nullptr);
-        }
-      }
-    }
-  };
-
-  load_a(0);
-  store_a(0);
-  load_b(0, rb0);
-  if (NKB > 1) load_b(1, rb1);
-  __syncthreads();
-  for (int kb = 0; kb < NKB; kb += 2) {
-    if (kb + 1 < NKB) load_a(kb + 1);
-    compute(0, rb0);
-    if (kb + 2 < NKB) load_b(kb + 2, rb0);
-    if (kb + 1 < NKB) store_a(1);
-    __syncthreads();
-    if (kb + 1 >= NKB) break;
-    if (kb + 2 < NKB) load_a(kb + 2);
-    compute(1, rb1);
-    if (kb + 3 < NKB) load_b(kb + 3, rb1);
-    if (kb + 2 < NKB) store_a(0);
-    __syncthreads();
-  }
-
   const int col = lane & 15, rg = (lane >> 4) * 4;
-  if (EPI == EPI_UP) {
-    if (!qok) return;
-    T* h = reinterpret_cast<T*>(g.h);
+  const uint4* Bw[PPW];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      if (mt >= n_mt) break;
+  for (int p = 0; p < PPW; ++p) {
+    const int q = min(q0 + p, g.NQ - 1);  // a pair past the end repeats the last one; not stored
+    Bw[p] = g.B + ((size_t)e * g.NQ + q) * (size_t)NKB * kPairUnits + lane;
+  }
+  uint4 ra[D][NMT][4], rb[D][PPW][8];
+  f32x4_t acc[PPW][NMT][2];
+#pragma unroll
+  for (int p = 0; p < PPW; ++p)
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) acc[p][mt][0] = acc[p][mt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  int kl = 0;  // next K block to load (stays at the last one once reached, when NKB < D)
+  auto load_w = [&](uint4(&b)[PPW][8]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int p = 0; p < PPW; ++p)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) b[p][u] = load_stream(Bw[p] + (size_t)kl * kPairUnits + u * kWave);
+  };
+  // The first weight blocks go out before anything that needs the item's row indices.
+  static_for<D>([&](auto sc) __attribute__((always_inline)) {
+    load_w(rb[decltype(sc)::value]);
+    kl += kl < NKB - 1 ? 1 : 0;
+  });
+
+  const uint4* ap[NMT];
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt) {
+    const int r = mt * 16 + (lane & 15);
+    const int rr = r < M ? r : 0;
+    int src;
+    if constexpr (EPI == EPI_UP) src = (e < g.E) ? g.row_tok[row0 + rr] : tok0 + rr;
+    else src = row0 + rr;
+    ap[mt] = reinterpret_cast<const uint4*>(g.A) + (size_t)src * row_units + (lane >> 4) * 4;
+  }
+  int ka = 0;  // next K block of activations to load
+  auto load_a = [&](uint4(&a)[NMT][4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) a[mt][s] = ap[mt][ka * kChunksPerRow + s];
+    ka += ka < NKB - 1 ? 1 : 0;
+  };
+  static_for<D>([&](auto sc) __attribute__((always_inline)) { load_a(ra[decltype(sc)::value]); });
+  // In the loop a stage's activations go out before its weights.
+  auto load = [&](uint4(&a)[NMT][4], uint4(&b)[PPW][8]) __attribute__((always_inline)) {
+    load_a(a);
+    load_w(b);
+    kl += kl < NKB - 1 ? 1 : 0;
+  };
+  auto compute = [&](const uint4(&a)[NMT][4], const uint4(&b)[PPW][8]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int p = 0; p < PPW; ++p)
+#pragma unroll
+        for (int mt = 0; mt < NMT; ++mt) {
+          mma_chunk(acc[p][mt][0], a[mt][s], b[p][s], (T*)nullptr);
+          mma_chunk(acc[p][mt][1], a[mt][s], b[p][4 + s], (T*)nullptr);
+        }
+  };
+
+  // Main loop: every load in it is in range (K block k0 + D + s < NKB). The tail then
+  // computes the last D..2D-1 blocks, loading the r = NKB - k0 - D not yet requested.
+  int k0 = 0;
+  for (; k0 + 2 * D <= NKB; k0 += D) {
+    static_for<D>([&](auto sc) __attribute__((always_inline)) {
+      constexpr int s = decltype(sc)::value;
+      compute(ra[s], rb[s]);
+      load(ra[s], rb[s]);
+      __builtin_amdgcn_sched_barrier(0);  // keep the loads here, D blocks ahead of their use
+    });
+  }
+  // DOWN: the ybuf row and gate of each accumulator row, requested before the last
+  // blocks' products so that their latency overlaps them.
+  int dst[EPI == EPI_DOWN ? NMT : 1][4];
+  float gate[EPI == EPI_DOWN ? NMT : 1][4];
+  if constexpr (EPI == EPI_DOWN) {
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = mt * 16 + rg + i;
-        if (r < M) {
-          const float gv = acc[mt][0][i], uv = acc[mt][1][i];
-          const float hv = gv / (1.0f + expf(-gv)) * uv;
-          store_elem(h, (size_t)(row0 + r) * g.I + q * 16 + col, hv);
+        const int r = min(mt * 16 + rg + i, M - 1);
+        if (e < g.E) {
+          dst[mt][i] = g.row_dst[row0 + r];
+          gate[mt][i] = g.row_gate[row0 + r];
+        } else {
+          dst[mt][i] = (tok0 + r) * g.KS + g.k + (e - g.E);
+          gate[mt][i] = 1.0f;
         }
       }
-    }
-  } else if (EPI == EPI_DOWN) {
-    if (!qok) return;
+  }
+  const int r = NKB - k0 - D;
+  static_for<D>([&](auto sc) __attribute__((always_inline)) {
+    constexpr int s = decltype(sc)::value;
+    if (k0 + s < NKB) compute(ra[s], rb[s]);
+    if (s < r) load(ra[s], rb[s]);
+  });
+  static_for<D - 1>([&](auto sc) __attribute__((always_inline)) {
+    constexpr int s = decltype(sc)::value;
+    if (s < r) compute(ra[s], rb[s]);
+  });
+
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      if (mt >= n_mt) break;
+  for (int p = 0; p < PPW; ++p) {
+    const int q = q0 + p;
+    if (q >= g.NQ) break;
+    if constexpr (EPI == EPI_UP) {
+      T* h = reinterpret_cast<T*>(g.h);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = mt * 16 + rg + i;
-        if (r < M) {
-          int dst;
-          float gate;
-          if (e < g.E) {
-            dst = g.row_dst[row0 + r];
-            gate = g.row_gate[row0 + r];
-          } else {
-            dst = (tok0 + r) * g.KS + g.k + (e - g.E);
-            gate = 1.0f;
+      for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = mt * 16 + rg + i;
+          if (r < M) {
+            const float gv = acc[p][mt][0][i], uv = acc[p][mt][1][i];
+            store_elem(h, (size_t)(row0 + r) * g.I + q * 16 + col, gv / (1.0f + expf(-gv)) * uv);
           }
-          float* yrow = g.ybuf + (size_t)dst * g.H + (2 * q) * 16 + col;
-          yrow[0] = acc[mt][0][i] * gate;
-          yrow[16] = acc[mt][1][i] * gate;
         }
-      }
-    }
-  } else {  // EPI_LM
-    const float NEG = -__builtin_huge_valf();
-    const int c0 = 2 * q * 16 + col, c1 = c0 + 16;
+    } else {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      if (mt >= n_mt) break;
+      for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (mt * 16 + rg + i < M) {
+            float* yrow = g.ybuf + (size_t)dst[mt][i] * g.H + (2 * q) * 16 + col;
+            yrow[0] = acc[p][mt][0][i] * gate[mt][i];
+            yrow[16] = acc[p][mt][1][i] * gate[mt][i];
+          }
+        }
+    }
+  }
+}
+
+// Expert GEMM over the device-built work list, PPW = g.ppw pairs per wavefront (chosen
+// on the host from the position count). Exactly the workgroups that carry work come
+// first (the grid is sized for the list's capacity; the rest leave at once), so all of
+// them are resident together; logical workgroups are laid out XCD by XCD (xcd_logical),
+// so the chunks of one item, and neighbouring items such as the row blocks of one
+// shared expert, share one L2. Logical wavefront lw takes chunk c = lw % chunks (pairs
+// [c*PPW, c*PPW + PPW)) of item lw / chunks.
+template <typename T, int EPI, int NMT, int D>
+__global__ __launch_bounds__(256, MV_GEMM_WAVES_PER_SIMD) void k_moe_gemm(GemmArgs g) {
+  const int chunks = (g.NQ + g.ppw - 1) / g.ppw;
+  const int n_items = *g.n_work;
+  const int n_wg = (n_items * chunks + kGemmWaves - 1) / kGemmWaves;
+  if ((int)blockIdx.x >= n_wg) return;  // workgroup-uniform
+  const int lw = xcd_logical((int)blockIdx.x, n_wg) * kGemmWaves + (threadIdx.x >> 6);
+  const int item = lw / chunks, c = lw - item * chunks;
+  if (item >= n_items) return;  // no barrier in this kernel
+  const int4 it = g.work[item];
+  const int q0 = c * g.ppw;
+  const bool one_tile = NMT > 1 && it.z <= 16;
+  if (g.ppw == 2) {
+    if (one_tile) moe_stream<T, EPI, 1, 2, D>(g, it.x, it.y, it.z, it.w, q0);
+    else moe_stream<T, EPI, NMT, 2, D>(g, it.x, it.y, it.z, it.w, q0);
+  } else {
+    if (one_tile) moe_stream<T, EPI, 1, 1, D + 1>(g, it.x, it.y, it.z, it.w, q0);
+    else moe_stream<T, EPI, NMT, 1, D + 1>(g, it.x, it.y, it.z, it.w, q0);
+  }
+}
+
+// LM head. A workgroup of 4 wavefronts covers 4*ppw consecutive column pairs (wavefront
+// w: pairs w*ppw ..) for one row block of up to 16*NMT <= kLmRows positions, so every
+// weight byte is read once per row block (at most 128 positions need one row block).
+// The block's normalised rows are staged in LDS one 256-byte K block at a time (double
+// buffered, read one K block ahead in registers) and shared by the 4 wavefronts.
+// Weights stream as in moe_stream, two K blocks in flight; no load in the main loop
+// depends on a branch.
+// After each pair, every row's 32 logits are reduced across the 16 column lanes to
+// (top-1 value, lowest index, top-2 value); lane c then folds into its running records
+// only the rows j*16 + c of its lane group's 4*NMT rows (so a lane keeps NMT/4 records,
+// not 4*NMT). At the end the records are merged across the 4 wavefronts and one record
+// per row and workgroup goes to part.
+template <typename T, int NMT>
+__device__ __forceinline__ void lm_stream(const GemmArgs& g, int row0, int M, int pg, int ppw,
+                                          uint4 (*As)[kLmRows][kChunksPerRow + 1],
+                                          Top2 (*red)[kLmRows]) {
+  constexpr int MB = NMT * 16;
+  constexpr int AL = MB * kChunksPerRow / 256;  // 16-byte A chunks per thread per K block
+  constexpr int NR = (4 * NMT + 15) / 16;       // running records per lane
+  static_assert(AL >= 1, "row blocks have at least 16 rows");
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int row_units = g.K * (int)sizeof(T) / 16;
+  const int NKB = row_units / kChunksPerRow;
+  const int col = lane & 15, rg = (lane >> 4) * 4;
+  const int q0 = (pg * kGemmWaves + wave) * ppw;
+  const float NEG = -__builtin_huge_valf();
+  const int F = ppw * NKB;
+
+  // A staging: thread -> (row srow + 16*j, chunk schunk) of the K block; AL chunks.
+  const int srow = threadIdx.x >> 4, schunk = threadIdx.x & 15;
+  const u32x4_t* abase = reinterpret_cast<const u32x4_t*>(g.A) + schunk;
+  int aoff[AL];  // 16-byte offset of each staged row (a block's rows past M repeat its first)
+#pragma unroll
+  for (int j = 0; j < AL; ++j) {
+    const int r = srow + 16 * j;
+    aoff[j] = (row0 + (r < M ? r : 0)) * row_units;
+  }
+  // A block f+1 waits in ra while block f is in LDS.
+  u32x4_t ra[AL];
+  int fa = 0, ka = 0;  // next A block: flat index (stops at the last) and K block in the row
+  auto read_a = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < AL; ++j) ra[j] = abase[aoff[j] + ka * kChunksPerRow];
+    const bool adv = fa < F - 1;
+    fa += adv ? 1 : 0;
+    ka = adv ? (ka + 1 == NKB ? 0 : ka + 1) : ka;
+  };
+  auto write_a = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < AL; ++j) *reinterpret_cast<u32x4_t*>(&As[buf][srow + 16 * j][schunk]) = ra[j];
+  };
+
+  // Pairs past the vocabulary's last pair stream a copy of it; their columns are masked.
+  const uint4* Bw = g.B + (size_t)min(q0, g.NQ - 1) * NKB * kPairUnits + lane;
+  const int nq_real = max(0, min(ppw, g.NQ - q0));
+  const int FB = max(1, nq_real) * NKB;  // K blocks with distinct weights for this wavefront
+  uint4 rb[2][8];
+  int fl = 0;
+  auto load_b = [&](uint4(&b)[8]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) b[u] = load_stream(Bw + (size_t)fl * kPairUnits + u * kWave);
+    fl += fl < FB - 1 ? 1 : 0;
+  };
+
+  f32x4_t acc[NMT][2];
+  Top2 best[NR];
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt) acc[mt][0] = acc[mt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < NR; ++j) best[j] = Top2{NEG, INT_MAX, NEG};
+  auto compute = [&](int buf, const uint4(&b)[8]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt) {
+        const uint4 a = As[buf][mt * 16 + (lane & 15)][(lane >> 4) * 4 + s];
+        mma_chunk(acc[mt][0], a, b[s], (T*)nullptr);
+        mma_chunk(acc[mt][1], a, b[4 + s], (T*)nullptr);
+      }
+  };
+  auto fold = [&](int q) __attribute__((always_inline)) {  // fold the finished pair q into the running records
+    const int c0 = 2 * q * 16 + col, c1 = c0 + 16;
+    const bool ok0 = q < g.NQ && c0 < g.n_valid, ok1 = q < g.NQ && c1 < g.n_valid;
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float v0 = (qok && c0 < g.n_valid) ? acc[mt][0][i] : NEG;
-        const float v1 = (qok && c1 < g.n_valid) ? acc[mt][1][i] : NEG;
-        Top2 rec;
-        if (v0 >= v1) { rec.v1 = v0; rec.i1 = c0; rec.v2 = v1; }
-        else { rec.v1 = v1; rec.i1 = c1; rec.v2 = v0; }
+        const float v0 = ok0 ? acc[mt][0][i] : NEG;
+        const float v1 = ok1 ? acc[mt][1][i] : NEG;
+        Top2 rec;  // this lane's two columns (c0 < c1: a tie keeps c0)
+        rec.v1 = fmaxf(v0, v1);
+        rec.i1 = v1 > v0 ? c1 : c0;
+        rec.v2 = fminf(v0, v1);
 #pragma unroll
         for (int m = 1; m < 16; m <<= 1) rec = top2_merge(rec, top2_shfl_xor(rec, m));
-        if (col == 0) red[wave][mt * 16 + rg + i] = rec;
+        const int j = mt * 4 + i;  // record j of this lane group: lane j % 16 keeps it
+        if (j % 16 == col) best[j / 16] = top2_merge(best[j / 16], rec);
       }
-    }
-    __syncthreads();
-    if ((int)threadIdx.x < M) {
-      const int r = threadIdx.x;
-      Top2 rec = red[0][r];
 #pragma unroll
-      for (int w = 1; w < kGemmWaves; ++w) rec = top2_merge(rec, red[w][r]);
-      g.part[(size_t)(row0 + r) * g.n_pg + pg] = rec;
+    for (int mt = 0; mt < NMT; ++mt) acc[mt][0] = acc[mt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  };
+
+  // prologue: A block 0 into LDS, block 1 into registers; B blocks 0 and 1. In every
+  // step the activation read goes out before the weight loads: waits are in issue
+  // order, so waiting for the activations then never waits for the newest weights.
+  read_a();
+  write_a(0);
+  read_a();
+  load_b(rb[0]);
+  load_b(rb[1]);
+  __syncthreads();
+  // Pair by pair, two K blocks per step (NKB is even, so LDS buffer and B register set
+  // of block kb are both kb & 1). Every load in the steps is in range: the last two
+  // blocks of the last pair are done apart, loading no weights. Activation reads past
+  // the last block repeat it (they are L2 hits and feed nothing).
+  for (int qi = 0; qi < ppw; ++qi) {
+    const bool last = qi == ppw - 1;
+    const int kend = last ? NKB - 2 : NKB;
+    for (int kb0 = 0; kb0 < kend; kb0 += 2) {
+      static_for<2>([&](auto sc) __attribute__((always_inline)) {
+        constexpr int s = decltype(sc)::value;
+        compute(s, rb[s]);
+        write_a(s ^ 1);
+        read_a();
+        load_b(rb[s]);
+        __syncthreads();
+      });
     }
+    if (last) {
+      static_for<2>([&](auto sc) __attribute__((always_inline)) {
+        constexpr int s = decltype(sc)::value;
+        compute(s, rb[s]);
+        if (s == 0) write_a(1);
+        __syncthreads();
+      });
+    }
+    fold(q0 + qi);
   }
+
+  // lane c of lane group g holds, in best[k], row (j/4)*16 + 4g + j%4 for j = 16k + c
+#pragma unroll
+  for (int k = 0; k < NR; ++k) {
+    const int j = 16 * k + col;
+    if (j < 4 * NMT) red[wave][(j / 4) * 16 + rg + (j % 4)] = best[k];
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < M) {
+    const int r = threadIdx.x;
+    Top2 rec = red[0][r];
+#pragma unroll
+    for (int w = 1; w < kGemmWaves; ++w) rec = top2_merge(rec, red[w][r]);
+    g.part[(size_t)(row0 + r) * g.n_pg + pg] = rec;
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256, 2) void k_lm_head(GemmArgs g) {
+  __shared__ uint4 As[2][kLmRows][kChunksPerRow + 1];
+  __shared__ Top2 red[kGemmWaves][kLmRows];
+  const int n_items = (g.Tn + kLmRows - 1) / kLmRows;
+  const int n = n_items * g.n_pg;
+  if ((int)blockIdx.x >= n) return;  // workgroup-uniform
+  // column-group major: the row blocks of one column group are logical neighbours, so
+  // they run side by side on one XCD and share its weight stream through L2
+  const int L = xcd_logical((int)blockIdx.x, n);
+  const int pg = L / n_items, item = L - pg * n_items;
+  const int row0 = item * kLmRows, M = min(kLmRows, g.Tn - row0);
+  const int ppw = g.lm_ppw;
+  if (M <= 16) lm_stream<T, 1>(g, row0, M, pg, ppw, As, red);
+  else if (M <= 32) lm_stream<T, 2>(g, row0, M, pg, ppw, As, red);
+  else if (M <= 64) lm_stream<T, 4>(g, row0, M, pg, ppw, As, red);
+  else lm_stream<T, 8>(g, row0, M, pg, ppw, As, red);
 }
 
 // ============================================================================ argmax, accept, combine
@@ -543,51 +826,68 @@ hipError_t launch_repack_router(const void* src, void* dst, int L, int E, int ro
   return hipGetLastError();
 }
 
+int norm_positions_per_wg(int Tn) { return Tn >= 4096 ? 16 : 4; }
+
+size_t norm_lds_bytes(int wdtype, int H, int np) {
+  return (size_t)np * (H * (wdtype == 1 ? 2 : 4) + 16) + (size_t)np * 64 * sizeof(float);
+}
+
+template <typename T, int NP, int VM>
+static void norm_route_t(bool route, const float* x_in, const float* ybuf, float* x_out, float* x_copy, void* a_out,
+                         const uint4* w, const float* bias, int32_t* topk_id, float* topk_w, int Tn, int H, int KS,
+                         int E, int k, float eps, hipStream_t stream) {
+  const dim3 grid((Tn + NP - 1) / NP), block(256);
+  const int wdtype = sizeof(T) == 2 ? 1 : 0;
+  if (route)
+    k_norm_route<T, true, NP, VM><<<grid, block, norm_lds_bytes(wdtype, H, NP), stream>>>(
+        x_in, ybuf, x_out, x_copy, static_cast<T*>(a_out), w, bias, topk_id, topk_w, Tn, H, KS, E, k, eps);
+  else
+    k_norm_route<T, false, NP, VM><<<grid, block, 0, stream>>>(x_in, ybuf, x_out, x_copy, static_cast<T*>(a_out), w,
+                                                               bias, topk_id, topk_w, Tn, H, KS, E, k, eps);
+}
+
+template <typename T, int NP>
+static void norm_route_np(bool route, const float* x_in, const float* ybuf, float* x_out, float* x_copy, void* a_out,
+                          const uint4* w, const float* bias, int32_t* topk_id, float* topk_w, int Tn, int H, int KS,
+                          int E, int k, float eps, hipStream_t stream) {
+  const int vm = (H / 4 + kWave - 1) / kWave;  // float4 per lane of one row
+  if (vm <= 2) norm_route_t<T, NP, 2>(route, x_in, ybuf, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, KS, E, k, eps, stream);
+  else if (vm == 5) norm_route_t<T, NP, 5>(route, x_in, ybuf, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, KS, E, k, eps, stream);
+  else if (vm <= 8) norm_route_t<T, NP, 8>(route, x_in, ybuf, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, KS, E, k, eps, stream);
+  else norm_route_t<T, NP, 16>(route, x_in, ybuf, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, KS, E, k, eps, stream);
+}
+
 hipError_t launch_norm_route(int wdtype, bool route, const float* x_in, const float* ybuf, float* x_out,
                              float* x_copy, void* a_out, const void* wr, const float* bias, int32_t* topk_id,
                              float* topk_w, int Tn, int H, int KS, int E, int k, float eps, hipStream_t stream) {
-  const dim3 grid((Tn + 3) / 4), block(256);
   const uint4* w = static_cast<const uint4*>(wr);
+  const bool big = norm_positions_per_wg(Tn) == 16;
   if (wdtype == 1) {
-    const size_t lds = route ? (size_t)4 * H * sizeof(uint16_t) : 0;
-    if (route)
-      k_norm_route<uint16_t, true><<<grid, block, lds, stream>>>(x_in, ybuf, x_out, x_copy,
-                                                                 static_cast<uint16_t*>(a_out), w, bias, topk_id,
-                                                                 topk_w, Tn, H, KS, E, k, eps);
-    else
-      k_norm_route<uint16_t, false><<<grid, block, 0, stream>>>(x_in, ybuf, x_out, x_copy,
-                                                                static_cast<uint16_t*>(a_out), w, bias, topk_id,
-                                                                topk_w, Tn, H, KS, E, k, eps);
+    if (big) norm_route_np<uint16_t, 16>(route, x_in, ybuf, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, KS, E, k, eps, stream);
+    else norm_route_np<uint16_t, 4>(route, x_in, ybuf, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, KS, E, k, eps, stream);
   } else {
-    const size_t lds = route ? (size_t)4 * H * sizeof(float) : 0;
-    if (route)
-      k_norm_route<float, true><<<grid, block, lds, stream>>>(x_in, ybuf, x_out, x_copy, static_cast<float*>(a_out),
-                                                              w, bias, topk_id, topk_w, Tn, H, KS, E, k, eps);
-    else
-      k_norm_route<float, false><<<grid, block, 0, stream>>>(x_in, ybuf, x_out, x_copy, static_cast<float*>(a_out),
-                                                             w, bias, topk_id, topk_w, Tn, H, KS, E, k, eps);
+    if (big) norm_route_np<float, 16>(route, x_in, ybuf, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, KS, E, k, eps, stream);
+    else norm_route_np<float, 4>(route, x_in, ybuf, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, KS, E, k, eps, stream);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_plan(const int32_t* topk_id, const float* topk_w, int Tn, int k, int E, int S, int32_t* row_tok,
-                       int32_t* row_dst, float* row_gate, int4* work, int32_t* n_work, int32_t* counts,
-                       hipStream_t stream) {
-  k_plan<<<1, 1024, 0, stream>>>(topk_id, topk_w, Tn, k, E, S, row_tok, row_dst, row_gate, work, n_work, counts);
+hipError_t launch_plan(const PlanArgs& pa, hipStream_t stream) {
+  k_plan<<<1, 1024, 0, stream>>>(pa);
   return hipGetLastError();
 }
 
-hipError_t launch_gemm(int wdtype, int epi, const GemmArgs& args, dim3 grid, hipStream_t stream) {
-  const dim3 block(256);
-  if (wdtype == 1) {
-    if (epi == EPI_UP) k_gemm<uint16_t, EPI_UP><<<grid, block, 0, stream>>>(args);
-    else if (epi == EPI_DOWN) k_gemm<uint16_t, EPI_DOWN><<<grid, block, 0, stream>>>(args);
-    else k_gemm<uint16_t, EPI_LM><<<grid, block, 0, stream>>>(args);
-  } else {
-    if (epi == EPI_UP) k_gemm<float, EPI_UP><<<grid, block, 0, stream>>>(args);
-    else if (epi == EPI_DOWN) k_gemm<float, EPI_DOWN><<<grid, block, 0, stream>>>(args);
-    else k_gemm<float, EPI_LM><<<grid, block, 0, stream>>>(args);
-  }
+template <typename T>
+static void gemm_t(int epi, const GemmArgs& args, unsigned n_wg, hipStream_t stream) {
+  const dim3 grid(n_wg), block(256);
+  if (epi == EPI_UP) k_moe_gemm<T, EPI_UP, MV_GEMM_NMT, MV_GEMM_D><<<grid, block, 0, stream>>>(args);
+  else if (epi == EPI_DOWN) k_moe_gemm<T, EPI_DOWN, MV_GEMM_NMT, MV_GEMM_D><<<grid, block, 0, stream>>>(args);
+  else k_lm_head<T><<<grid, block, 0, stream>>>(args);
+}
+
+hipError_t launch_gemm(int wdtype, int epi, const GemmArgs& args, unsigned n_wg, hipStream_t stream) {
+  if (wdtype == 1) gemm_t<uint16_t>(epi, args, n_wg, stream);
+  else gemm_t<float>(epi, args, n_wg, stream);
   return hipGetLastError();
 }
 

@@ -1,0 +1,168 @@
+"""Summaries of rocprofv3 output for the measurement notes (kernel trace and HBM counters).
+
+    python -m lossless_speculative_verification_amd.profiling trace DB
+        per-kernel launch count and duration statistics of a --kernel-trace database
+        (rocpd SQLite), steady state of the verify step included;
+    python -m lossless_speculative_verification_amd.profiling traffic --workload W \\
+            --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR --copy-bytes N --out FILE
+        per-launch HBM bytes of every kernel from two --pmc runs (FETCH_SIZE, then
+        WRITE_SIZE; rocprofv3 csv output) of the bench, each scaled by what the same
+        counter reads for a plain copy of N bytes (--copy-calibration mode of bench.py).
+
+The traffic file records the sha256 of the kernel sources; bench.py reports a kernel's
+traffic only while that hash still matches the sources (counters of an older build
+would describe other kernels).
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import glob
+import hashlib
+import os
+import re
+import sqlite3
+import statistics
+from typing import Dict, Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG, "csrc")
+TRAFFIC_RE = re.compile(r"^traffic_bytes_per_launch\s+(\S+)\s+(\d+)\s+fetch\s+(\d+)\s+write\s+(\d+)\s+sha256\s+(\w+)")
+
+
+def source_sha() -> str:
+    """sha256 over the HIP sources and headers the library is built from."""
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.h"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode())
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def short_name(name: str) -> str:
+    n = name.split("(")[0].replace("void ", "").replace("mv::", "")
+    return n.replace("unsigned short", "bf16")
+
+
+def trace_table(db_path: str) -> str:
+    """Markdown table: kernel, calls, avg/min/max/total microseconds, grid, registers."""
+    db = sqlite3.connect(db_path)
+    rows = db.execute(
+        "select name, count(*), avg(end-start)/1000.0, min(end-start)/1000.0, max(end-start)/1000.0, "
+        "sum(end-start)/1000.0, max(grid_x), max(vgpr_count), max(accum_vgpr_count), max(lds_size) "
+        "from kernels group by name order by sum(end-start) desc").fetchall()
+    out = ["| kernel | calls | avg us | min us | max us | total us | grid (threads) | vgpr/agpr | lds B |",
+           "|---|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        out.append(f"| `{short_name(r[0])[:60]}` | {r[1]} | {r[2]:.2f} | {r[3]:.2f} | {r[4]:.2f} | {r[5]:.1f} | "
+                   f"{r[6]} | {r[7]}/{r[8]} | {r[9]} |")
+    return "\n".join(out)
+
+
+def step_breakdown(db_path: str, marker: str = "k_accept") -> str:
+    """Per-kernel medians within whole verify steps (a step ends with the acceptance kernel)."""
+    db = sqlite3.connect(db_path)
+    rows = db.execute("select name, start, end from kernels order by start").fetchall()
+    acc = [i for i, r in enumerate(rows) if short_name(r[0]).startswith(marker)]
+    steps = [rows[a + 1:b + 1] for a, b in zip(acc[:-1], acc[1:])]
+    if not steps:
+        return "(no complete steps in the trace)"
+    n = collections.Counter(len(s) for s in steps).most_common(1)[0][0]
+    steps = [s for s in steps if len(s) == n]
+    durs = collections.defaultdict(list)
+    for s in steps:
+        for name, a, b in s:
+            durs[short_name(name)].append((b - a) / 1000.0)
+    spans = [(s[-1][2] - s[0][1]) / 1000.0 for s in steps]
+    out = [f"{len(steps)} steps of {n} kernels; step span median {statistics.median(spans):.1f} us "
+           f"(first kernel start to acceptance end)", "",
+           "| kernel | launches/step | median us | us/step |", "|---|---|---|---|"]
+    for k, v in durs.items():
+        per = len(v) // len(steps)
+        out.append(f"| `{k[:60]}` | {per} | {statistics.median(v):.2f} | {sum(v) / len(steps):.1f} |")
+    return "\n".join(out)
+
+
+def counter_medians(csv_dir: str) -> Dict[str, float]:
+    """Median counter value (as rocprofv3 reports it) per kernel name, from a --pmc csv run."""
+    paths = glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not paths:
+        raise FileNotFoundError(f"no *counter_collection.csv under {csv_dir}")
+    vals = collections.defaultdict(list)
+    for p in paths:
+        with open(p) as f:
+            for r in csv.DictReader(f):
+                vals[short_name(r["Kernel_Name"])].append(float(r["Counter_Value"]))
+    return {k: statistics.median(v) for k, v in vals.items()}
+
+
+def copy_scale(csv_dir: str, copy_bytes: int) -> float:
+    """Bytes per counter unit: the copy's true bytes over the largest counter reading."""
+    med = counter_medians(csv_dir)
+    reading = max(med.values())
+    return copy_bytes / reading
+
+
+def read_traffic(path: str, kernel_prefix: str) -> Optional[dict]:
+    """Traffic record of the first kernel starting with kernel_prefix, if the file's source
+    hash matches the current sources; else None."""
+    if not os.path.exists(path):
+        return None
+    sha = source_sha()
+    with open(path) as f:
+        for line in f:
+            m = TRAFFIC_RE.match(line.strip().strip("`"))
+            if m and m.group(1).startswith(kernel_prefix) and m.group(5) == sha:
+                return {"kernel": m.group(1), "bytes": int(m.group(2)), "fetch": int(m.group(3)),
+                        "write": int(m.group(4))}
+    return None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("db")
+    r = sub.add_parser("traffic")
+    r.add_argument("--workload", required=True)
+    r.add_argument("--fetch", required=True)
+    r.add_argument("--write", required=True)
+    r.add_argument("--copy-fetch", required=True)
+    r.add_argument("--copy-write", required=True)
+    r.add_argument("--copy-bytes", type=int, required=True)
+    r.add_argument("--out", required=True)
+    r.add_argument("--command", default="")
+    args = ap.parse_args()
+    if args.cmd == "trace":
+        print(trace_table(args.db))
+        print()
+        print(step_breakdown(args.db))
+        return
+    fs = copy_scale(args.copy_fetch, args.copy_bytes)
+    ws = copy_scale(args.copy_write, args.copy_bytes)
+    fetch = counter_medians(args.fetch)
+    write = counter_medians(args.write)
+    sha = source_sha()
+    lines = [f"# HBM traffic per launch: {args.workload}", "",
+             "FETCH_SIZE and WRITE_SIZE medians per kernel launch, each scaled by what the same counter "
+             f"reads for a plain copy of {args.copy_bytes} bytes (bytes per counter unit: fetch {fs:.1f}, "
+             f"write {ws:.1f}).", ""]
+    if args.command:
+        lines += ["Commands (repo root, one MI355X):", "", "```", args.command, "```", ""]
+    lines += ["| kernel | fetch bytes | write bytes | total |", "|---|---|---|---|"]
+    recs = []
+    for k in sorted(set(fetch) | set(write), key=lambda k: -(fetch.get(k, 0) * fs + write.get(k, 0) * ws)):
+        fb, wb = int(fetch.get(k, 0) * fs), int(write.get(k, 0) * ws)
+        lines.append(f"| `{k[:60]}` | {fb} | {wb} | {fb + wb} |")
+        recs.append(f"traffic_bytes_per_launch {k.replace(' ', '')} {fb + wb} fetch {fb} write {wb} sha256 {sha}")
+    lines += ["", "Machine-readable lines (kernel, bytes per launch, source hash of the build measured):", "", "```"]
+    lines += recs + ["```", ""]
+    with open(args.out, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+
+
+if __name__ == "__main__":
+    main()

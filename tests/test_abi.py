@@ -50,6 +50,8 @@ def test_valid_configs_pass(lib):
     real = _cfg(hidden=1280, n_routed=64, top_k=6, n_shared=2, inter=896, n_layers=12, vocab=129280,
                 wdtype=bnd.MOE_BF16, max_positions=36992)
     assert lib.moe_verify_check_config(ctypes.byref(real)) == bnd.MOE_OK
+    for h, wd in ((4096, bnd.MOE_BF16), (2048, bnd.MOE_F32)):  # the largest hidden sizes covered
+        assert lib.moe_verify_check_config(ctypes.byref(_cfg(hidden=h, inter=128, wdtype=wd))) == bnd.MOE_OK
     assert bnd.last_error() == ""
 
 
@@ -69,6 +71,8 @@ def test_valid_configs_pass(lib):
     (dict(hidden=100), bnd.MOE_EUNSUPPORTED),
     (dict(inter=96), bnd.MOE_EUNSUPPORTED),
     (dict(hidden=192, wdtype=bnd.MOE_BF16), bnd.MOE_EUNSUPPORTED),
+    (dict(hidden=4224, inter=128, wdtype=bnd.MOE_BF16), bnd.MOE_EUNSUPPORTED),  # above 4096 (bf16)
+    (dict(hidden=2112), bnd.MOE_EUNSUPPORTED),                        # above 2048 (f32)
     (dict(max_positions=10_000_000), bnd.MOE_EUNSUPPORTED),
 ])
 def test_bad_configs_rejected(lib, kw, code):
