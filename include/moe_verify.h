@@ -66,8 +66,9 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 /* Host struct. Shapes the kernels cover (else MOE_EUNSUPPORTED):
  *   1 <= n_routed <= 64 (one wavefront lane per routed expert), 1 <= top_k <= n_routed,
  *   0 <= n_shared <= 8, n_layers >= 1, vocab >= 0,
- *   hidden and inter multiples of 128 (bf16) or 64 (f32), hidden <= 4096 (bf16) or
- *   2048 (f32), inter <= 16384, max_positions >= 1. */
+ *   hidden and inter multiples of 128 (bf16) or 64 (f32), and hidden a multiple of 256
+ *   (bf16) or 128 (f32) when vocab > 0; hidden <= 4096 (bf16) or 2048 (f32),
+ *   inter <= 16384, max_positions >= 1. */
 typedef struct {
   int32_t hidden;        /* H                                                        */
   int32_t n_routed;      /* E routed experts                                         */

@@ -41,11 +41,22 @@ int kblock_elems(int32_t wdtype) { return mv::kRowBlockBytes / elem_bytes(wdtype
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Upper bound on GEMM work items for T positions (each routed expert's rows split in
-// blocks of kGemmMB, plus at most one partial block per expert, plus the shared blocks).
-int64_t max_work_items(const moe_verify_config& c, int64_t T) {
-  const int64_t mb = mv::kGemmMB;
+// Upper bound on GEMM work items of at most mb rows for T positions (each routed
+// expert's rows split in blocks of mb, plus at most one partial block per expert, plus
+// the shared blocks).
+int64_t max_work_items(const moe_verify_config& c, int64_t T, int64_t mb = mv::kGemmMB) {
   return (T * c.top_k + mb - 1) / mb + c.n_routed + (int64_t)c.n_shared * ((T + mb - 1) / mb);
+}
+
+// Passes of at least this many positions run the expert GEMMs on the LDS-tiled kernel
+// (bf16 weights, contractions of at least 256 elements): work items of up to kTileM rows
+// then keep the matrix cores busy, while smaller passes are bound by the weight stream
+// and use the streaming kernel.
+#ifndef MV_TILED_MIN_POSITIONS
+#define MV_TILED_MIN_POSITIONS 256
+#endif
+bool use_tiled(const moe_verify_config& c, int Tn) {
+  return c.wdtype == MOE_BF16 && Tn >= MV_TILED_MIN_POSITIONS && c.hidden >= 256 && c.inter >= 256;
 }
 
 int check_config(const moe_verify_config* c) {
@@ -64,6 +75,10 @@ int check_config(const moe_verify_config* c) {
   if (c->hidden % kb || c->inter % kb)
     return fail(MOE_EUNSUPPORTED, "hidden %d and inter %d must be multiples of %d for this dtype", c->hidden,
                 c->inter, kb);
+  // the LM head pipelines the contraction two 256-byte blocks at a time
+  if (c->vocab > 0 && c->hidden % (2 * kb))
+    return fail(MOE_EUNSUPPORTED, "with an LM head, hidden %d must be a multiple of %d for this dtype", c->hidden,
+                2 * kb);
   // hidden: one residual row is held in 16 float4 per lane; the router's LDS rows fit 64 KB
   if (c->hidden > (c->wdtype == MOE_BF16 ? 4096 : 2048) || c->inter > 16384)
     return fail(MOE_EUNSUPPORTED, "hidden %d (max %d for this dtype) or inter %d (max 16384) too large", c->hidden,
@@ -123,10 +138,10 @@ struct moe_verify_ctx {
   int32_t* topk_id = nullptr;
   float* topk_w = nullptr;
   int32_t* row_tok = nullptr;
-  int32_t* row_dst = nullptr;
-  float* row_gate = nullptr;
+  int32_t* slot_row = nullptr;  // routed row of each slot (inverse of the expert-major order)
   int4* work = nullptr;
   int32_t* n_work = nullptr;
+  int32_t* chunk_cnt = nullptr;  // [chunks][64] expert counts per slot chunk (large-pass plan)
   void* h = nullptr;
   float* ybuf = nullptr;
   mv::Top2* part = nullptr;
@@ -179,21 +194,24 @@ namespace {
 int run_block(moe_verify_ctx* c, int l, const float* x_in, const float* ybuf_prev, int Tn, hipStream_t st) {
   const moe_verify_config& g = c->cfg;
   const int E = g.n_routed, S = g.n_shared, k = g.top_k, KS = k + S, H = g.hidden, I = g.inter;
-  const int wmax = (int)max_work_items(g, Tn);
+  const bool tiled = use_tiled(g, Tn);
+  const int mb = tiled ? mv::kTileM : mv::kGemmMB;
+  const int wmax = (int)max_work_items(g, Tn, mb);
   mv::PlanArgs pa{};
   pa.topk_id = c->topk_id;
   pa.topk_w = c->topk_w;
   pa.Tn = Tn; pa.k = k; pa.E = E; pa.S = S;
   pa.row_tok = c->row_tok;
-  pa.row_dst = c->row_dst;
-  pa.row_gate = c->row_gate;
+  pa.slot_row = c->slot_row;
   pa.work = c->work;
   pa.n_work = c->n_work;
   pa.counts = c->counts + (size_t)l * E;
+  pa.mb = mb;
+  pa.chunk_cnt = c->chunk_cnt;
   c->prof_begin(MOE_PROF_NORM_ROUTE, st);
-  MV_CHECK(mv::launch_norm_route(g.wdtype, true, x_in, ybuf_prev, c->x_ws, nullptr, c->a,
+  MV_CHECK(mv::launch_norm_route(g.wdtype, true, x_in, ybuf_prev, c->slot_row, c->x_ws, nullptr, c->a,
                                  c->router_p + l * c->router_units_per_layer, c->bias_p + (size_t)l * 64, c->topk_id,
-                                 c->topk_w, Tn, H, KS, E, k, g.rms_eps, st));
+                                 c->topk_w, Tn, H, S, E, k, g.rms_eps, tiled, st));
   c->prof_end(st);
   c->prof_begin(MOE_PROF_PLAN, st);
   MV_CHECK(mv::launch_plan(pa, st));
@@ -204,17 +222,21 @@ int run_block(moe_verify_ctx* c, int l, const float* x_in, const float* ybuf_pre
   a.Tn = Tn;
   a.k = k; a.E = E; a.KS = KS; a.H = H; a.I = I;
   a.row_tok = c->row_tok;
-  a.row_dst = c->row_dst;
-  a.row_gate = c->row_gate;
   a.max_items = wmax;
-  // Two pairs per wavefront when the expected items x pairs fill at least one round of
-  // resident wavefronts (routed items: one per touched expert while positions are few).
+  a.sink_row = g.max_positions * KS;  // the extra row past every real row of h and ybuf
+  // Streaming kernel: two pairs per wavefront when the expected items x pairs fill at
+  // least one round of resident wavefronts (routed items: one per touched expert while
+  // positions are few).
   const int wave_target = c->n_cu * mv::kGemmWaves * MV_GEMM_WAVES_PER_SIMD;
-  const int mb = mv::kGemmMB;
   const int est_items = std::min(E, Tn * k) + S * ((Tn + mb - 1) / mb);
-  auto chunks_for = [&](int NQ, int* ppw) {
+  auto grid_for = [&](int NQ, int* ppw) -> unsigned {
+    if (tiled) return (unsigned)c->n_cu;  // persistent: one workgroup per compute unit
     *ppw = est_items * NQ >= wave_target ? 2 : 1;
-    return (NQ + *ppw - 1) / *ppw;
+    const int chunks = (NQ + *ppw - 1) / *ppw;
+    return (unsigned)((wmax * chunks + mv::kGemmWaves - 1) / mv::kGemmWaves);
+  };
+  auto launch = [&](int epi, unsigned n_wg) {
+    return tiled ? mv::launch_gemm_tiled(epi, a, n_wg, st) : mv::launch_gemm(g.wdtype, epi, a, n_wg, st);
   };
   // gate/up + SwiGLU
   a.A = c->a;
@@ -223,8 +245,8 @@ int run_block(moe_verify_ctx* c, int l, const float* x_in, const float* ybuf_pre
   a.NQ = c->NQ_up;
   a.h = c->h;
   c->prof_begin(MOE_PROF_GEMM_UP, st);
-  int ch = chunks_for(c->NQ_up, &a.ppw);
-  MV_CHECK(mv::launch_gemm(g.wdtype, mv::EPI_UP, a, (unsigned)((wmax * ch + mv::kGemmWaves - 1) / mv::kGemmWaves), st));
+  unsigned n_wg = grid_for(c->NQ_up, &a.ppw);
+  MV_CHECK(launch(mv::EPI_UP, n_wg));
   c->prof_end(st);
   // down + gate scale
   a.A = c->h;
@@ -233,8 +255,8 @@ int run_block(moe_verify_ctx* c, int l, const float* x_in, const float* ybuf_pre
   a.NQ = c->NQ_dn;
   a.ybuf = c->ybuf;
   c->prof_begin(MOE_PROF_GEMM_DOWN, st);
-  ch = chunks_for(c->NQ_dn, &a.ppw);
-  MV_CHECK(mv::launch_gemm(g.wdtype, mv::EPI_DOWN, a, (unsigned)((wmax * ch + mv::kGemmWaves - 1) / mv::kGemmWaves), st));
+  n_wg = grid_for(c->NQ_dn, &a.ppw);
+  MV_CHECK(launch(mv::EPI_DOWN, n_wg));
   c->prof_end(st);
   return MOE_OK;
 }
@@ -310,12 +332,13 @@ MV_API int moe_verify_init(const moe_verify_config* cfg, const moe_verify_weight
   A(&c->topk_id, P * k * sizeof(int32_t));
   A(&c->topk_w, P * k * sizeof(float));
   A(&c->row_tok, P * k * sizeof(int32_t));
-  A(&c->row_dst, P * k * sizeof(int32_t));
-  A(&c->row_gate, P * k * sizeof(float));
+  A(&c->slot_row, P * k * sizeof(int32_t));
   A(&c->work, wmax * sizeof(int4));
   A(&c->n_work, sizeof(int32_t));
-  A(&c->h, P * KS * I * es);
-  A(&c->ybuf, P * KS * H * sizeof(float));
+  A(&c->chunk_cnt, (size_t)mv::plan_chunks(g.max_positions, k) * 64 * sizeof(int32_t));
+  // h and ybuf rows: every slot's row plus one sink row for the tiled GEMM's padding stores
+  A(&c->h, (P * KS + 1) * I * es);
+  A(&c->ybuf, (P * KS + 1) * H * sizeof(float));
   if (g.vocab > 0) A(&c->part, P * c->n_pg_lm * sizeof(mv::Top2));
   A(&c->counts, (size_t)L * E * sizeof(int32_t));
   if (ae != hipSuccess) {
@@ -369,8 +392,9 @@ MV_API int moe_verify_step(moe_verify_ctx* c, const float* hidden_in, int32_t B,
   }
   const int KS = g.top_k + g.n_shared;
   c->prof_begin(MOE_PROF_NORM_ROUTE, st);
-  MV_CHECK(mv::launch_norm_route(g.wdtype, false, c->x_ws, c->ybuf, nullptr, hidden_out, c->a, nullptr, nullptr,
-                                 nullptr, nullptr, Tn, g.hidden, KS, g.n_routed, g.top_k, g.rms_eps, st));
+  MV_CHECK(mv::launch_norm_route(g.wdtype, false, c->x_ws, c->ybuf, c->slot_row, nullptr, hidden_out,
+                                 g.vocab > 0 ? c->a : nullptr, nullptr, nullptr, nullptr, c->topk_w, Tn, g.hidden,
+                                 g.n_shared, g.n_routed, g.top_k, g.rms_eps, false, st));
   c->prof_end(st);
   if (g.vocab > 0) {
     // Workgroups (4 wavefronts, two per CU) cover one row block of up to kLmRows
@@ -423,7 +447,7 @@ MV_API int moe_verify_debug_layer(moe_verify_ctx* c, int32_t layer, const float*
   int rc = run_block(c, layer, x_in, nullptr, T, st);
   if (rc) return rc;
   const int KS = g.top_k + g.n_shared;
-  if (moe_out) MV_CHECK(mv::launch_combine(c->ybuf, T, g.hidden, KS, moe_out, st));
+  if (moe_out) MV_CHECK(mv::launch_combine(c->ybuf, c->slot_row, c->topk_w, T, g.hidden, g.top_k, g.n_shared, moe_out, st));
   const size_t kb = (size_t)T * g.top_k * 4;
   if (topk_id) MV_CHECK(hipMemcpyAsync(topk_id, c->topk_id, kb, hipMemcpyDeviceToDevice, st));
   if (topk_w) MV_CHECK(hipMemcpyAsync(topk_w, c->topk_w, kb, hipMemcpyDeviceToDevice, st));

@@ -26,6 +26,9 @@ constexpr int kGemmWaves = 4;                       // waves per GEMM workgroup 
 #endif
 constexpr int kGemmMB = 16 * MV_GEMM_NMT;           // rows per expert GEMM work item
 constexpr int kLmRows = 128;                        // positions per LM-head row block
+constexpr int kTileM = 256;                         // rows per work item of the LDS-tiled expert GEMM
+constexpr int kPlanChunk = 2048;                    // routed slots per workgroup of the large-pass plan
+constexpr int kPlanSingleMaxChunks = 8;             // up to this many chunks one workgroup plans alone
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -40,6 +43,15 @@ __device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int
 template <int N, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Stage-ordered row layout of bf16 activation rows, read by the LDS-tiled expert GEMM:
+// within each 256-byte block of a row, the 16-byte chunk c = 4*g + s (s = c % 4) is
+// stored at chunk position 4*s + g, so the four chunks one MFMA step contracts (chunks
+// 4*g + s, g = 0..3) are 64 contiguous bytes. Element index of element e of a row.
+__device__ __forceinline__ int stage_ordered_elem(int e) {
+  const int c = (e >> 3) & 15;
+  return (e & ~127) | ((((c & 3) << 2) | (c >> 2)) << 3) | (e & 7);
 }
 
 // bf16 is carried as uint16_t bit patterns.
@@ -89,6 +101,13 @@ __device__ __forceinline__ uint4 load_stream(const uint4* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// SwiGLU of one gate/up pair, silu(g) * u with silu(g) = g / (1 + e^-g), from the
+// hardware exponential and reciprocal (a few ulp of float32, far below the bf16 rounding
+// the result gets; e^-g overflowing to infinity gives a reciprocal of exactly 0).
+__device__ __forceinline__ float swiglu(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
+
 // Top-1/top-2 record for the argmax reductions: value, lowest index, second value.
 struct Top2 {
   float v1;
@@ -121,6 +140,17 @@ __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
   return v;
+}
+
+// Logical workgroup index of hardware workgroup h when the first n carry work.
+// Workgroups are dealt to the 8 XCDs round-robin; here each XCD takes one contiguous
+// range of logical indices instead, so logical neighbours (the row blocks of one expert,
+// which stream the same weights) share one L2.
+__device__ __forceinline__ int xcd_logical(int h, int n) {
+  const int x = h & 7, j = h >> 3;
+  int start = 0;
+  for (int y = 0; y < x; ++y) start += (n - y + 7) >> 3;
+  return start + j;
 }
 
 }  // namespace mv

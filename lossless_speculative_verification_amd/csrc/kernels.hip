@@ -89,15 +89,24 @@ __device__ __forceinline__ void store4(uint16_t* p, size_t i4, float4 u) {
   w.y = f32_to_bf16(u.z) | (f32_to_bf16(u.w) << 16);
   reinterpret_cast<uint2*>(p)[i4] = w;
 }
+// The same four elements at their place in the stage-ordered row layout (see
+// stage_ordered_elem): the four stay together inside one 16-byte chunk.
+__device__ __forceinline__ void store4_perm(float* p, size_t i4, float4 u) { store4(p, i4, u); }
+__device__ __forceinline__ void store4_perm(uint16_t* p, size_t i4, float4 u) {
+  store4(p, stage_ordered_elem((int)i4 * 4) / 4, u);
+}
 
 // One workgroup of four wavefronts handles NP consecutive positions; VM float4 per lane
 // hold one residual row (H <= 256 * VM).
-//  1. (wavefront per position) x = x_in + (y_0 + ... + y_{KS-1}) with the previous
-//     block's per-slot outputs summed in slot order (absent for the first block); x is
+//  1. (wavefront per position) x = x_in + (g_0 y_0 + ... + g_{k-1} y_{k-1} + y_k + ...
+//     + y_{k+S-1}): the previous block's expert outputs of the position's slots, routed
+//     ones (rows slot_row[t*k + j], gates topk_w) then shared ones (gate 1), summed in
+//     slot order (absent for the first block); x is
 //     written back as the residual stream (and to x_copy when given). The slot rows are
 //     read SB at a time with all their loads in flight together.
 //  2. a = x / sqrt(mean(x^2) + eps), stored in the element type (bf16 rounding) to a_out
-//     and, for routing, to LDS.
+//     (in the stage-ordered row layout when perm_a, for the tiled expert GEMM) and, for
+//     routing, to LDS.
 //  3. (route) router logits for the NP positions as a small MFMA product: wavefront w
 //     computes experts 16w..16w+15 against all NP rows (the 16-row MFMA tile repeats
 //     row 0 in its unused rows, whose results are dropped), float32 accumulation. The
@@ -110,11 +119,12 @@ __device__ __forceinline__ void store4(uint16_t* p, size_t i4, float4 u) {
 // flight at the join): indices past the end are clamped and their values masked.
 template <typename T, bool ROUTE, int NP, int VM>
 __global__ __launch_bounds__(256) void k_norm_route(const float* x_in, const float* __restrict__ ybuf,
+                                                    const int32_t* __restrict__ slot_row,
                                                     float* x_out, float* __restrict__ x_copy,
                                                     T* __restrict__ a_out, const uint4* __restrict__ wr,
                                                     const float* __restrict__ bias,
                                                     int32_t* __restrict__ topk_id, float* __restrict__ topk_w,
-                                                    int Tn, int H, int KS, int E, int k, float eps) {
+                                                    int Tn, int H, int S, int E, int k, float eps, int perm_a) {
   constexpr int SB = VM <= 5 ? 8 : 4;  // slot rows read together
   constexpr int RB = 20;               // router K chunks (64 bytes of a row each) per load batch
   extern __shared__ uint4 lds_raw[];
@@ -141,26 +151,35 @@ __global__ __launch_bounds__(256) void k_norm_route(const float* x_in, const flo
     const float4* xi = reinterpret_cast<const float4*>(x_in) + (size_t)t * H4;
     float4 v[VM];
     if (ybuf) {
-      const float4* yb = reinterpret_cast<const float4*>(ybuf) + (size_t)t * KS * H4;
+      const float4* yb = reinterpret_cast<const float4*>(ybuf);
+      const int KS = k + S;
       float4 m[VM];
 #pragma unroll
       for (int j = 0; j < VM; ++j) m[j] = make_float4(0.f, 0.f, 0.f, 0.f);
       for (int s0 = 0; s0 < KS; s0 += SB) {
         float4 y[SB][VM];
+        float gt[SB];
 #pragma unroll
-        for (int s = 0; s < SB; ++s)
+        for (int s = 0; s < SB; ++s) {
+          const int sl = min(s0 + s, KS - 1);  // slot: routed j < k (its gate), then shared (gate 1)
+          const int jr = min(sl, k - 1);
+          const int rr = slot_row[(size_t)t * k + jr];
+          const float gr = topk_w[(size_t)t * k + jr];
+          const size_t row = sl < k ? (size_t)rr : (size_t)Tn * k + (size_t)(sl - k) * Tn + t;
+          gt[s] = sl < k ? gr : 1.0f;
 #pragma unroll
-          for (int j = 0; j < VM; ++j)
-            y[s][j] = yb[(size_t)min(s0 + s, KS - 1) * H4 + min(lane + kWave * j, H4 - 1)];
+          for (int j = 0; j < VM; ++j) y[s][j] = yb[row * H4 + min(lane + kWave * j, H4 - 1)];
+        }
 #pragma unroll
         for (int s = 0; s < SB; ++s)
 #pragma unroll
           for (int j = 0; j < VM; ++j) {
             const bool ok = s0 + s < KS && lane + kWave * j < H4;
-            m[j].x += ok ? y[s][j].x : 0.f;
-            m[j].y += ok ? y[s][j].y : 0.f;
-            m[j].z += ok ? y[s][j].z : 0.f;
-            m[j].w += ok ? y[s][j].w : 0.f;
+            // one fused multiply-add per slot, as in k_combine (same results bit for bit)
+            m[j].x = ok ? fmaf(gt[s], y[s][j].x, m[j].x) : m[j].x;
+            m[j].y = ok ? fmaf(gt[s], y[s][j].y, m[j].y) : m[j].y;
+            m[j].z = ok ? fmaf(gt[s], y[s][j].z, m[j].z) : m[j].z;
+            m[j].w = ok ? fmaf(gt[s], y[s][j].w, m[j].w) : m[j].w;
           }
       }
 #pragma unroll
@@ -190,7 +209,10 @@ __global__ __launch_bounds__(256) void k_norm_route(const float* x_in, const flo
       const int i = lane + kWave * j;
       if (i < H4) {
         const float4 u = make_float4(v[j].x * inv, v[j].y * inv, v[j].z * inv, v[j].w * inv);
-        store4(a_out + (size_t)t * H, i, u);
+        if (a_out) {
+          if (perm_a) store4_perm(a_out + (size_t)t * H, i, u);
+          else store4(a_out + (size_t)t * H, i, u);
+        }
         if (ROUTE) store4(lrow, i, u);
       }
     }
@@ -259,83 +281,72 @@ __global__ __launch_bounds__(256) void k_norm_route(const float* x_in, const flo
 
 // ============================================================================ routing plan
 
-// The routing plan, computed by one workgroup of NW wavefronts: it orders the T*k routed
-// slots (slot = t*k + j) by expert, stably (ascending slot within an expert), and lists
-// the GEMM work items.
-//  phase 1: per-wavefront expert histograms of NW contiguous slot segments;
-//  phase 2: exclusive scan in (expert, segment) order -> each segment's write base;
-//  phase 3: each wavefront places its segment 64 slots at a time; lanes with the same
-//           expert are found with six ballots over the expert id bits, and a lane's
-//           rank is the count of lower lanes in its group;
-//  phase 4: work items of at most kGemmMB rows: each shared expert's position blocks
-//           first (so the blocks of one shared expert are neighbours in the item list),
-//           then the routed experts' row blocks in expert order.
-// Routed rows occupy [0, T*k) of the row space; shared expert s owns rows
-// T*k + s*T + t.
+// The routing plan orders the T*k routed slots (slot = t*k + j) by expert, stably
+// (ascending slot within an expert), and lists the GEMM work items. Routed rows occupy
+// [0, T*k) of the row space in that order; shared expert s owns rows T*k + s*T + t.
+// Work items (expert, first row, rows, first token) have at most pa.mb rows: each shared
+// expert's position blocks first (so the blocks of one shared expert are neighbours in
+// the item list), then the routed experts' row blocks in expert order.
+//
+// Building blocks, for a workgroup of NW wavefronts that owns slots [beg, end):
+//  seg_hist:    per-wavefront expert histograms of NW contiguous sub-segments;
+//  seg_cursors: exclusive scan in (expert, sub-segment) order from the per-expert write
+//               base of the workgroup's range -> each sub-segment's write cursor;
+//  seg_scatter: each wavefront places its sub-segment 64 slots at a time; lanes with the
+//               same expert are found with six ballots over the expert id bits, and a
+//               lane's rank is the count of lower lanes in its group.
+// One workgroup plans a small pass alone (k_plan); a large pass is cut into chunks whose
+// expert counts are taken first (k_plan_count), after which every chunk knows its write
+// base and is placed by its own workgroup (k_plan_scatter).
+
+constexpr int kPlanBatch = 8;  // slots per lane whose loads are in flight together
 
 template <int NW>
-__device__ void plan_body(const PlanArgs& pa, int (*hist)[64], int* off, int* wstart) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int E = pa.E, S = pa.S, k = pa.k, Tn = pa.Tn;
-  const int N = Tn * k, KS = k + S;
+__device__ void seg_hist(const PlanArgs& pa, int beg, int end, int (*hist)[64]) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int N = pa.Tn * pa.k;
   hist[wave][lane] = 0;
   __syncthreads();
-
-  // Each wavefront reads its segment PB*64 slots at a time, all loads of a batch in
-  // flight together (one memory round trip per batch rather than per 64 slots).
-  constexpr int PB = 8;
-  const int seg = (N + NW - 1) / NW;
-  const int beg = min(N, wave * seg), end = min(N, beg + seg);
-  for (int b0 = beg; b0 < end; b0 += PB * kWave) {
-    int key[PB];
+  const int seg = (end - beg + NW - 1) / NW;
+  const int b = min(end, beg + wave * seg), e = min(end, b + seg);
+  for (int b0 = b; b0 < e; b0 += kPlanBatch * kWave) {
+    int key[kPlanBatch];
 #pragma unroll
-    for (int u = 0; u < PB; ++u) key[u] = pa.topk_id[min(b0 + u * kWave + lane, N - 1)];
+    for (int u = 0; u < kPlanBatch; ++u) key[u] = pa.topk_id[min(b0 + u * kWave + lane, N - 1)];
 #pragma unroll
-    for (int u = 0; u < PB; ++u)
-      if (b0 + u * kWave + lane < end) atomicAdd(&hist[wave][min(max(key[u], 0), E - 1)], 1);
+    for (int u = 0; u < kPlanBatch; ++u)
+      if (b0 + u * kWave + lane < e) atomicAdd(&hist[wave][min(max(key[u], 0), pa.E - 1)], 1);
   }
   __syncthreads();
+}
 
-  if (wave == 0) {
-    int c = 0;
-    if (lane < E)
-      for (int w = 0; w < NW; ++w) c += hist[w][lane];
-    const int nb = (c + kGemmMB - 1) / kGemmMB;
-    // inclusive scans over lanes of c and nb
-    int sc = c, sn = nb;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int oc = __shfl_up(sc, d, kWave), on = __shfl_up(sn, d, kWave);
-      if (lane >= d) { sc += oc; sn += on; }
-    }
-    off[lane] = sc - c;
-    wstart[lane] = sn - nb;
-    if (lane < E) pa.counts[lane] = c;
-    if (lane == 63) { off[64] = sc; wstart[64] = sn; }
-    int run = sc - c;
-    for (int w = 0; w < NW; ++w) {
-      const int h = hist[w][lane];
-      hist[w][lane] = run;  // becomes the segment's write cursor for this expert
-      run += h;
-    }
+// Wavefront 0, lane = expert: hist[w][e] becomes sub-segment w's first row for expert e.
+template <int NW>
+__device__ void seg_cursors(int (*hist)[64], int base) {
+  int run = base;
+  for (int w = 0; w < NW; ++w) {
+    const int h = hist[w][threadIdx.x];
+    hist[w][threadIdx.x] = run;
+    run += h;
   }
-  __syncthreads();
+}
 
-  for (int b0 = beg; b0 < end; b0 += PB * kWave) {
-    int keys[PB];
-    float gates[PB];
+template <int NW>
+__device__ void seg_scatter(const PlanArgs& pa, int beg, int end, int (*hist)[64]) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int N = pa.Tn * pa.k, k = pa.k;
+  const int seg = (end - beg + NW - 1) / NW;
+  const int b = min(end, beg + wave * seg), e = min(end, b + seg);
+  for (int b0 = b; b0 < e; b0 += kPlanBatch * kWave) {
+    int keys[kPlanBatch];
 #pragma unroll
-    for (int u = 0; u < PB; ++u) {
-      const int i = min(b0 + u * kWave + lane, N - 1);
-      keys[u] = pa.topk_id[i];
-      gates[u] = pa.topk_w[i];
-    }
+    for (int u = 0; u < kPlanBatch; ++u) keys[u] = pa.topk_id[min(b0 + u * kWave + lane, N - 1)];
 #pragma unroll
-    for (int u = 0; u < PB; ++u) {
+    for (int u = 0; u < kPlanBatch; ++u) {
       const int i = b0 + u * kWave + lane;
-      if (b0 + u * kWave >= end) break;  // wavefront-uniform
-      const bool active = i < end;
-      const int key = active ? min(max(keys[u], 0), E - 1) : 0;  // ids come from k_norm_route, always < E
+      if (b0 + u * kWave >= e) break;  // wavefront-uniform
+      const bool active = i < e;
+      const int key = active ? min(max(keys[u], 0), pa.E - 1) : 0;  // ids come from k_norm_route, always < E
       unsigned long long mask = __ballot(active);
 #pragma unroll
       for (int bit = 0; bit < 6; ++bit) {
@@ -351,47 +362,109 @@ __device__ void plan_body(const PlanArgs& pa, int (*hist)[64], int* off, int* ws
       if (active) {
         const int tok = i / k, j = i - tok * k;
         pa.row_tok[pos] = tok;
-        pa.row_dst[pos] = tok * KS + j;
-        pa.row_gate[pos] = gates[u];
+        pa.slot_row[i] = pos;
         if (rank == cnt - 1) hist[wave][key] = pos + 1;
       }
       __builtin_amdgcn_wave_barrier();
     }
   }
+}
 
-  const int mbT = (Tn + kGemmMB - 1) / kGemmMB;
-  const int nsw = S * mbT;  // shared-expert items come first
-  for (int idx = tid; idx < nsw; idx += NW * kWave) {
-    const int s = idx / mbT, b = idx - s * mbT;
-    pa.work[idx] = make_int4(E + s, N + s * Tn + b * kGemmMB, min(kGemmMB, Tn - b * kGemmMB), b * kGemmMB);
+// Wavefront 0, lane = expert, holding the expert's routed-row count c: first rows (off)
+// and first work items (wstart) by inclusive lane scans, per-expert counts out.
+__device__ void expert_offsets(const PlanArgs& pa, int c, int* off, int* wstart, bool write_counts) {
+  const int lane = threadIdx.x & 63;
+  const int nb = (c + pa.mb - 1) / pa.mb;
+  int sc = c, sn = nb;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int oc = __shfl_up(sc, d, kWave), on = __shfl_up(sn, d, kWave);
+    if (lane >= d) { sc += oc; sn += on; }
   }
-  if (tid < E) {
-    const int c = off[tid + 1] - off[tid];
-    for (int b = 0; b * kGemmMB < c; ++b)
-      pa.work[nsw + wstart[tid] + b] = make_int4(tid, off[tid] + b * kGemmMB, min(kGemmMB, c - b * kGemmMB), 0);
+  off[lane] = sc - c;
+  wstart[lane] = sn - nb;
+  if (write_counts && lane < pa.E) pa.counts[lane] = c;
+  if (lane == 63) { off[64] = sc; wstart[64] = sn; }
+}
+
+// Work items from the expert offsets (any number of threads).
+__device__ void write_work(const PlanArgs& pa, const int* off, const int* wstart, int nthreads) {
+  const int tid = threadIdx.x, mb = pa.mb, Tn = pa.Tn, N = pa.Tn * pa.k;
+  const int mbT = (Tn + mb - 1) / mb;
+  const int nsw = pa.S * mbT;  // shared-expert items come first
+  for (int idx = tid; idx < nsw; idx += nthreads) {
+    const int s = idx / mbT, b = idx - s * mbT;
+    pa.work[idx] = make_int4(pa.E + s, N + s * Tn + b * mb, min(mb, Tn - b * mb), b * mb);
+  }
+  for (int e = tid; e < pa.E; e += nthreads) {  // one thread per expert
+    const int c = off[e + 1] - off[e];
+    for (int b = 0; b * mb < c; ++b)
+      pa.work[nsw + wstart[e] + b] = make_int4(e, off[e] + b * mb, min(mb, c - b * mb), 0);
   }
   if (tid == 0) *pa.n_work = nsw + wstart[64];
 }
 
 __global__ __launch_bounds__(1024) void k_plan(PlanArgs pa) {
-  __shared__ int hist[16][64];
+  constexpr int NW = 16;
+  __shared__ int hist[NW][64];
   __shared__ int off[65];
   __shared__ int wstart[65];
-  plan_body<16>(pa, hist, off, wstart);
+  const int N = pa.Tn * pa.k;
+  seg_hist<NW>(pa, 0, N, hist);
+  if (threadIdx.x < kWave) {
+    int c = 0;
+    if ((int)threadIdx.x < pa.E)
+      for (int w = 0; w < NW; ++w) c += hist[w][threadIdx.x];
+    expert_offsets(pa, c, off, wstart, true);
+    seg_cursors<NW>(hist, off[threadIdx.x]);
+  }
+  __syncthreads();
+  seg_scatter<NW>(pa, 0, N, hist);
+  write_work(pa, off, wstart, NW * kWave);
+}
+
+// Large pass, step 1: chunk c's routed-slot count per expert -> chunk_cnt[c][64].
+__global__ __launch_bounds__(256) void k_plan_count(PlanArgs pa) {
+  constexpr int NW = 4;
+  __shared__ int hist[NW][64];
+  const int N = pa.Tn * pa.k;
+  const int beg = min(N, (int)blockIdx.x * kPlanChunk), end = min(N, beg + kPlanChunk);
+  seg_hist<NW>(pa, beg, end, hist);
+  if (threadIdx.x < 64) {
+    int c = 0;
+    for (int w = 0; w < NW; ++w) c += hist[w][threadIdx.x];
+    pa.chunk_cnt[blockIdx.x * 64 + threadIdx.x] = c;
+  }
+}
+
+// Large pass, step 2: chunk c's write base per expert is the expert's first row plus the
+// counts of chunks < c; workgroup 0 also writes the per-expert counts and the work list.
+__global__ __launch_bounds__(256) void k_plan_scatter(PlanArgs pa) {
+  constexpr int NW = 4;
+  __shared__ int hist[NW][64];
+  __shared__ int off[65];
+  __shared__ int wstart[65];
+  const int N = pa.Tn * pa.k;
+  const int beg = min(N, (int)blockIdx.x * kPlanChunk), end = min(N, beg + kPlanChunk);
+  seg_hist<NW>(pa, beg, end, hist);
+  if (threadIdx.x < kWave) {
+    const int e = threadIdx.x;
+    int tot = 0, pre = 0;
+    for (int c = 0; c < (int)gridDim.x; ++c) {
+      const int v = pa.chunk_cnt[c * 64 + e];
+      tot += v;
+      pre += c < (int)blockIdx.x ? v : 0;
+    }
+    if (e >= pa.E) tot = 0;
+    expert_offsets(pa, tot, off, wstart, blockIdx.x == 0);
+    seg_cursors<NW>(hist, off[e] + pre);
+  }
+  __syncthreads();
+  seg_scatter<NW>(pa, beg, end, hist);
+  if (blockIdx.x == 0) write_work(pa, off, wstart, NW * kWave);
 }
 
 // ============================================================================ grouped MFMA GEMM
-
-// Logical workgroup index of hardware workgroup h when the first n carry work.
-// Workgroups are dealt to the 8 XCDs round-robin; here each XCD takes one contiguous
-// range of logical indices instead, so logical neighbours (the row blocks of one expert,
-// which stream the same weights) share one L2.
-__device__ __forceinline__ int xcd_logical(int h, int n) {
-  const int x = h & 7, j = h >> 3;
-  int start = 0;
-  for (int y = 0; y < x; ++y) start += (n - y + 7) >> 3;
-  return start + j;
-}
 
 // One wavefront computes PPW consecutive column pairs (2 x 16 output columns each) of one
 // expert work item (up to 16*NMT rows) over the whole contraction, the pairs side by
@@ -408,8 +481,9 @@ __device__ __forceinline__ int xcd_logical(int h, int n) {
 // load in flight. The epilogue follows the loop:
 //   UP:   tile t = 0 is the gate projection, t = 1 the up projection of the same 16
 //         intermediate columns; the epilogue forms silu(gate) * up and stores it.
-//   DOWN: the epilogue scales by the row's gate (1 for shared experts) and writes the
-//         row's own ybuf slot; no two wavefronts write the same element.
+//   DOWN: the epilogue writes the row's expert output to the same row of ybuf (the gate
+//         is applied where the slots are summed); no two wavefronts write the same
+//         element.
 // There is no LDS and no barrier: wavefronts run free.
 template <typename T, int EPI, int NMT, int PPW, int D>
 __device__ __forceinline__ void moe_stream(const GemmArgs& g, int e, int row0, int M, int tok0, int q0) {
@@ -490,25 +564,6 @@ __device__ __forceinline__ void moe_stream(const GemmArgs& g, int e, int row0, i
       __builtin_amdgcn_sched_barrier(0);  // keep the loads here, D blocks ahead of their use
     });
   }
-  // DOWN: the ybuf row and gate of each accumulator row, requested before the last
-  // blocks' products so that their latency overlaps them.
-  int dst[EPI == EPI_DOWN ? NMT : 1][4];
-  float gate[EPI == EPI_DOWN ? NMT : 1][4];
-  if constexpr (EPI == EPI_DOWN) {
-#pragma unroll
-    for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = min(mt * 16 + rg + i, M - 1);
-        if (e < g.E) {
-          dst[mt][i] = g.row_dst[row0 + r];
-          gate[mt][i] = g.row_gate[row0 + r];
-        } else {
-          dst[mt][i] = (tok0 + r) * g.KS + g.k + (e - g.E);
-          gate[mt][i] = 1.0f;
-        }
-      }
-  }
   const int r = NKB - k0 - D;
   static_for<D>([&](auto sc) __attribute__((always_inline)) {
     constexpr int s = decltype(sc)::value;
@@ -533,7 +588,7 @@ __device__ __forceinline__ void moe_stream(const GemmArgs& g, int e, int row0, i
           const int r = mt * 16 + rg + i;
           if (r < M) {
             const float gv = acc[p][mt][0][i], uv = acc[p][mt][1][i];
-            store_elem(h, (size_t)(row0 + r) * g.I + q * 16 + col, gv / (1.0f + expf(-gv)) * uv);
+            store_elem(h, (size_t)(row0 + r) * g.I + q * 16 + col, swiglu(gv, uv));
           }
         }
     } else {
@@ -541,10 +596,11 @@ __device__ __forceinline__ void moe_stream(const GemmArgs& g, int e, int row0, i
       for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          if (mt * 16 + rg + i < M) {
-            float* yrow = g.ybuf + (size_t)dst[mt][i] * g.H + (2 * q) * 16 + col;
-            yrow[0] = acc[p][mt][0][i] * gate[mt][i];
-            yrow[16] = acc[p][mt][1][i] * gate[mt][i];
+          const int r = mt * 16 + rg + i;
+          if (r < M) {
+            float* yrow = g.ybuf + (size_t)(row0 + r) * g.H + (2 * q) * 16 + col;
+            yrow[0] = acc[p][mt][0][i];
+            yrow[16] = acc[p][mt][1][i];
           }
         }
     }
@@ -787,16 +843,22 @@ __global__ void k_accept(const int32_t* __restrict__ drafts, const int32_t* __re
 }
 
 // m[t] = sum_j ybuf[t][j] in slot order (the block output before the residual add).
-__global__ void k_combine(const float* __restrict__ ybuf, int Tn, int H, int KS, float* __restrict__ m) {
+__global__ void k_combine(const float* __restrict__ ybuf, const int32_t* __restrict__ slot_row,
+                          const float* __restrict__ gate, int Tn, int H, int k, int S, float* __restrict__ m) {
   const int H4 = H >> 2;
   const size_t total = (size_t)Tn * H4;
   for (size_t u = (size_t)blockIdx.x * blockDim.x + threadIdx.x; u < total; u += (size_t)gridDim.x * blockDim.x) {
     const size_t t = u / H4, i = u % H4;
-    const float4* yb = reinterpret_cast<const float4*>(ybuf) + t * KS * H4 + i;
-    float4 s = yb[0];
-    for (int j = 1; j < KS; ++j) {
-      const float4 y = yb[(size_t)j * H4];
-      s.x += y.x; s.y += y.y; s.z += y.z; s.w += y.w;
+    const float4* yb = reinterpret_cast<const float4*>(ybuf);
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < k + S; ++j) {
+      const size_t row = j < k ? (size_t)slot_row[t * k + j] : (size_t)Tn * k + (size_t)(j - k) * Tn + t;
+      const float gt = j < k ? gate[t * k + j] : 1.0f;
+      const float4 y = yb[row * H4 + i];
+      s.x = fmaf(gt, y.x, s.x);
+      s.y = fmaf(gt, y.y, s.y);
+      s.z = fmaf(gt, y.z, s.z);
+      s.w = fmaf(gt, y.w, s.w);
     }
     reinterpret_cast<float4*>(m)[u] = s;
   }
@@ -833,47 +895,60 @@ size_t norm_lds_bytes(int wdtype, int H, int np) {
 }
 
 template <typename T, int NP, int VM>
-static void norm_route_t(bool route, const float* x_in, const float* ybuf, float* x_out, float* x_copy, void* a_out,
-                         const uint4* w, const float* bias, int32_t* topk_id, float* topk_w, int Tn, int H, int KS,
-                         int E, int k, float eps, hipStream_t stream) {
+static void norm_route_t(bool route, const float* x_in, const float* ybuf, const int32_t* slot_row, float* x_out,
+                         float* x_copy, void* a_out, const uint4* w, const float* bias, int32_t* topk_id,
+                         float* topk_w, int Tn, int H, int S, int E, int k, float eps, int perm_a,
+                         hipStream_t stream) {
   const dim3 grid((Tn + NP - 1) / NP), block(256);
   const int wdtype = sizeof(T) == 2 ? 1 : 0;
   if (route)
     k_norm_route<T, true, NP, VM><<<grid, block, norm_lds_bytes(wdtype, H, NP), stream>>>(
-        x_in, ybuf, x_out, x_copy, static_cast<T*>(a_out), w, bias, topk_id, topk_w, Tn, H, KS, E, k, eps);
+        x_in, ybuf, slot_row, x_out, x_copy, static_cast<T*>(a_out), w, bias, topk_id, topk_w, Tn, H, S, E, k, eps,
+        perm_a);
   else
-    k_norm_route<T, false, NP, VM><<<grid, block, 0, stream>>>(x_in, ybuf, x_out, x_copy, static_cast<T*>(a_out), w,
-                                                               bias, topk_id, topk_w, Tn, H, KS, E, k, eps);
+    k_norm_route<T, false, NP, VM><<<grid, block, 0, stream>>>(x_in, ybuf, slot_row, x_out, x_copy,
+                                                               static_cast<T*>(a_out), w, bias, topk_id, topk_w, Tn,
+                                                               H, S, E, k, eps, perm_a);
 }
 
 template <typename T, int NP>
-static void norm_route_np(bool route, const float* x_in, const float* ybuf, float* x_out, float* x_copy, void* a_out,
-                          const uint4* w, const float* bias, int32_t* topk_id, float* topk_w, int Tn, int H, int KS,
-                          int E, int k, float eps, hipStream_t stream) {
+static void norm_route_np(bool route, const float* x_in, const float* ybuf, const int32_t* slot_row, float* x_out,
+                          float* x_copy, void* a_out, const uint4* w, const float* bias, int32_t* topk_id,
+                          float* topk_w, int Tn, int H, int S, int E, int k, float eps, int perm_a,
+                          hipStream_t stream) {
   const int vm = (H / 4 + kWave - 1) / kWave;  // float4 per lane of one row
-  if (vm <= 2) norm_route_t<T, NP, 2>(route, x_in, ybuf, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, KS, E, k, eps, stream);
-  else if (vm == 5) norm_route_t<T, NP, 5>(route, x_in, ybuf, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, KS, E, k, eps, stream);
-  else if (vm <= 8) norm_route_t<T, NP, 8>(route, x_in, ybuf, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, KS, E, k, eps, stream);
-  else norm_route_t<T, NP, 16>(route, x_in, ybuf, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, KS, E, k, eps, stream);
+  if (vm <= 2) norm_route_t<T, NP, 2>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, stream);
+  else if (vm == 5) norm_route_t<T, NP, 5>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, stream);
+  else if (vm <= 8) norm_route_t<T, NP, 8>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, stream);
+  else norm_route_t<T, NP, 16>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, stream);
 }
 
-hipError_t launch_norm_route(int wdtype, bool route, const float* x_in, const float* ybuf, float* x_out,
-                             float* x_copy, void* a_out, const void* wr, const float* bias, int32_t* topk_id,
-                             float* topk_w, int Tn, int H, int KS, int E, int k, float eps, hipStream_t stream) {
+hipError_t launch_norm_route(int wdtype, bool route, const float* x_in, const float* ybuf,
+                             const int32_t* slot_row, float* x_out, float* x_copy, void* a_out, const void* wr,
+                             const float* bias, int32_t* topk_id, float* topk_w, int Tn, int H, int S, int E,
+                             int k, float eps, bool perm_a, hipStream_t stream) {
   const uint4* w = static_cast<const uint4*>(wr);
   const bool big = norm_positions_per_wg(Tn) == 16;
   if (wdtype == 1) {
-    if (big) norm_route_np<uint16_t, 16>(route, x_in, ybuf, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, KS, E, k, eps, stream);
-    else norm_route_np<uint16_t, 4>(route, x_in, ybuf, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, KS, E, k, eps, stream);
+    if (big) norm_route_np<uint16_t, 16>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, stream);
+    else norm_route_np<uint16_t, 4>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, stream);
   } else {
-    if (big) norm_route_np<float, 16>(route, x_in, ybuf, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, KS, E, k, eps, stream);
-    else norm_route_np<float, 4>(route, x_in, ybuf, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, KS, E, k, eps, stream);
+    if (big) norm_route_np<float, 16>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, stream);
+    else norm_route_np<float, 4>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, stream);
   }
   return hipGetLastError();
 }
 
+int plan_chunks(int Tn, int k) { return (Tn * k + kPlanChunk - 1) / kPlanChunk; }
+
 hipError_t launch_plan(const PlanArgs& pa, hipStream_t stream) {
-  k_plan<<<1, 1024, 0, stream>>>(pa);
+  const int n = plan_chunks(pa.Tn, pa.k);
+  if (n <= kPlanSingleMaxChunks || !pa.chunk_cnt) {
+    k_plan<<<1, 1024, 0, stream>>>(pa);
+  } else {
+    k_plan_count<<<n, 256, 0, stream>>>(pa);
+    k_plan_scatter<<<n, 256, 0, stream>>>(pa);
+  }
   return hipGetLastError();
 }
 
@@ -903,8 +978,9 @@ hipError_t launch_accept(const int32_t* drafts, const int32_t* argmax, int B, in
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const float* ybuf, int Tn, int H, int KS, float* m, hipStream_t stream) {
-  k_combine<<<grid_for((size_t)Tn * (H / 4), 256), 256, 0, stream>>>(ybuf, Tn, H, KS, m);
+hipError_t launch_combine(const float* ybuf, const int32_t* slot_row, const float* gate, int Tn, int H, int k,
+                          int S, float* m, hipStream_t stream) {
+  k_combine<<<grid_for((size_t)Tn * (H / 4), 256), 256, 0, stream>>>(ybuf, slot_row, gate, Tn, H, k, S, m);
   return hipGetLastError();
 }
 

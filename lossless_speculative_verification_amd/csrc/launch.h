@@ -15,12 +15,13 @@ struct PlanArgs {
   const int32_t* topk_id;
   const float* topk_w;
   int Tn, k, E, S;
-  int32_t* row_tok;
-  int32_t* row_dst;
-  float* row_gate;
+  int32_t* row_tok;   // out: token of each routed row
+  int32_t* slot_row;  // out: routed row of each slot t*k + j
   int4* work;
   int32_t* n_work;
   int32_t* counts;
+  int mb;              // rows per work item
+  int32_t* chunk_cnt;  // [chunks][64] scratch of the large-pass plan, or NULL (one workgroup)
 };
 
 // Arguments of the expert GEMMs and the LM head (see k_moe_gemm, k_lm_head in kernels.hip).
@@ -36,14 +37,13 @@ struct GemmArgs {
   int Tn;                  // positions in this pass
   int k, E, KS, H, I;      // top-k, routed experts, k + shared, hidden, intermediate
   void* h;                 // UP out: h[rows][I]
-  const int32_t* row_dst;  // DOWN: ybuf row of each routed row
-  const float* row_gate;   // DOWN: gate of each routed row
-  float* ybuf;             // DOWN out: ybuf[T][KS][H]
+  float* ybuf;             // DOWN out: ybuf[rows][H], row r = the expert output of row r of h
   Top2* part;              // LM out: part[T][n_pg]
   int n_pg;                // LM: workgroups along the vocabulary (each 4 * lm_ppw pairs)
   int lm_ppw;              // LM: column pairs per wavefront
   int ppw;                 // expert GEMMs: column pairs per wavefront (1 or 2)
   int max_items;           // expert GEMMs: capacity of the work list (grid covers max_items x chunks)
+  int sink_row;            // tiled expert GEMMs: row of h / ybuf that takes the stores of padding rows
 };
 
 hipError_t launch_repack_pairs(const void* src0, const void* src1, void* dst, int n_mats, int N,
@@ -51,14 +51,25 @@ hipError_t launch_repack_pairs(const void* src0, const void* src1, void* dst, in
                                hipStream_t stream);
 hipError_t launch_repack_router(const void* src, void* dst, int L, int E, int row_bytes,
                                 hipStream_t stream);
-// Combine + residual + RMSNorm (+ router and top-k when route).
-hipError_t launch_norm_route(int wdtype, bool route, const float* x_in, const float* ybuf, float* x_out,
-                             float* x_copy, void* a_out, const void* wr, const float* bias,
-                             int32_t* topk_id, float* topk_w, int Tn, int H, int KS, int E, int k,
-                             float eps, hipStream_t stream);
+// Combine of the previous block (ybuf rows gathered through slot_row, gates from topk_w)
+// + residual + RMSNorm (+ router and top-k when route, overwriting topk_id/topk_w);
+// a_out in the stage-ordered row layout when perm_a (bf16 only).
+hipError_t launch_norm_route(int wdtype, bool route, const float* x_in, const float* ybuf,
+                             const int32_t* slot_row, float* x_out, float* x_copy, void* a_out, const void* wr,
+                             const float* bias, int32_t* topk_id, float* topk_w, int Tn, int H, int S, int E,
+                             int k, float eps, bool perm_a, hipStream_t stream);
+// Routing plan: one workgroup for up to kPlanSingleMaxChunks chunks of kPlanChunk slots
+// (or when chunk_cnt is NULL), else a count pass and a scatter pass of one workgroup
+// per chunk.
 hipError_t launch_plan(const PlanArgs& pa, hipStream_t stream);
+int plan_chunks(int Tn, int k);
 // One-dimensional grid of n_wg workgroups (item x column-pair group, see k_gemm).
 hipError_t launch_gemm(int wdtype, int epi, const GemmArgs& args, unsigned n_wg, hipStream_t stream);
+// LDS-tiled expert GEMM (bf16) over work items of up to kTileM rows and
+// tiled_tiles_per_item(NQ) column tiles each; n_wg persistent workgroups (one per compute
+// unit) share the tiles. Needs K >= 256 elements.
+hipError_t launch_gemm_tiled(int epi, const GemmArgs& args, unsigned n_wg, hipStream_t stream);
+int tiled_tiles_per_item(int NQ);
 // Positions per workgroup of the norm/router kernel and its dynamic LDS bytes.
 int norm_positions_per_wg(int Tn);
 size_t norm_lds_bytes(int wdtype, int H, int np);
@@ -66,6 +77,8 @@ hipError_t launch_argmax_reduce(const Top2* part, int n_pg, int Tn, int32_t* arg
                                 hipStream_t stream);
 hipError_t launch_accept(const int32_t* drafts, const int32_t* argmax, int B, int K, int32_t* accepted,
                          int32_t* committed, hipStream_t stream);
-hipError_t launch_combine(const float* ybuf, int Tn, int H, int KS, float* m, hipStream_t stream);
+// m[t] = sum_j gate[t][j] * ybuf[slot_row[t*k + j]] + sum_s ybuf[T*k + s*T + t].
+hipError_t launch_combine(const float* ybuf, const int32_t* slot_row, const float* gate, int Tn, int H, int k,
+                          int S, float* m, hipStream_t stream);
 
 }  // namespace mv

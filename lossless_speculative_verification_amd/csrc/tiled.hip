@@ -1,0 +1,307 @@
+// Expert GEMMs for passes with many positions per expert (prefill-sized passes):
+// an LDS-tiled grouped MFMA GEMM over work items of up to kTileM rows of one expert.
+//
+// The products are those of the verify step's MoE block (pages: "jina-ocr-v1" model page,
+// architecture paragraph: 64 routed + 2 shared SwiGLU experts, top-6 routing):
+//   UP:   h = bf16(silu(A W_gate^T) * (A W_up^T)) for the expert's rows of A
+//   DOWN: y = h W_down^T, written to the same row of ybuf as the row of h
+// with the same row space, work list, outputs and float32 accumulation as the
+// streaming kernels (k_moe_gemm), so either path can run any block.
+#include "launch.h"
+
+namespace mv {
+
+// Tile: kTileM rows x kTilePairs column pairs (256 output columns; for UP the pairs are
+// (gate tile q, up tile q), i.e. 128 intermediate columns). 8 wavefronts (two per SIMD)
+// in a 2 x 4 grid: wavefront (wm, wn) owns rows 128*wm.. and the pairs 2*wn, 2*wn + 1,
+// i.e. 8 x 4 MFMA tiles of 16x16 (128 accumulator registers).
+//
+// The contraction advances one MFMA step (32 elements) per stage: stage st is step
+// s = st % 4 of the 256-byte K block kb = st / 4 of the pair layout, in which lane group
+// g = l / 16 contracts the 16-byte chunk g*4 + s of the block. LDS holds a stage as
+// 16-byte units in exactly the order the MFMA reads them:
+//   A unit (mt, l):   row 16*mt + l % 16 of the item, chunk (l/16)*4 + s of block kb
+//   B unit (p, t, l): pair-layout unit (t, s, l) of block kb of pair p of the tile
+// so every LDS read of a wavefront is 1 KB contiguous (no bank conflicts), and every
+// 1 KB run is filled by one wavefront-wide direct global-to-LDS load (lane l's 16 bytes
+// land at unit l of the run): wavefront w fills A row tiles w and w + 8 and the B runs
+// (p, t) = ((w + 8r) / 2, w % 2), r = 0, 1 — four loads per wavefront per stage.
+//
+// The MFMA takes the weights as its first operand and the activations as its second, so
+// lane l of a 16x16 result holds position 16*i + l % 16 and the four consecutive output
+// columns 4*(l/16)..+3: the epilogue stores 8 bytes (UP, bf16) or 16 bytes (DOWN, fp32)
+// per lane and row, no LDS round trip.
+//
+// Pipeline: kTileStages = 4 LDS stages in a ring. Step st multiplies stage st from
+// registers while stage st + 1's operands are read from LDS and stages st + 2 .. st + 4
+// are in flight to LDS: after waiting for this wavefront's loads of stage st + 1 and its
+// LDS reads of stage st, a barrier makes stage st + 1 visible and frees the slot of
+// stage st, into which stage st + 4 is requested. The loads write LDS without passing
+// through registers, so the registers hold only the accumulators and two steps'
+// operands. The waits are explicit (the compiler does not count these loads), and the
+// barrier is a plain s_barrier that is also a compiler memory barrier: no load or LDS
+// access moves across it, and it does not wait for the loads in flight.
+constexpr int kTilePairs = 8;
+constexpr int kTileThreads = 512;
+constexpr int kTileStages = 4;
+constexpr int kRunUnits = kWave;       // 16-byte units per 1 KB run
+constexpr int kStageRuns = 16;         // runs per operand per stage
+constexpr int kLoadsPerStage = 4;      // direct loads per wavefront per stage
+constexpr int kUpStores = 16;          // epilogue stores per wavefront: UP 8 rows x 2 pairs
+constexpr int kDownStores = 32;        //   DOWN 8 rows x 2 pairs x 2 tiles
+
+// s_waitcnt for at most N vector-memory operations of this wavefront still in flight and
+// none of its LDS operations (expcnt left unconstrained).
+template <int N>
+__device__ __forceinline__ void wait_vmem_lds() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+// Direct global-to-LDS loads (lane l's 16 or 4 bytes land at lds + 16*l or 4*l; lds is
+// wavefront-uniform and goes to M0). Written as assembly so that the compiler does not
+// track them: it would otherwise drain every such load in flight before any LDS read it
+// cannot prove disjoint from them. Their completion is covered by the explicit waits
+// above; M0 is used by nothing else in these kernels.
+__device__ __forceinline__ void lds_load16(const void* gptr, const void* lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(gptr) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_load4(const void* gptr, const void* lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(m0), "v"(gptr) : "memory", "m0");
+}
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+template <int EPI>
+__global__ __launch_bounds__(kTileThreads, 1) void k_moe_tiled(GemmArgs g) {
+  constexpr int NST = EPI == EPI_UP ? kUpStores : kDownStores;
+  constexpr int STAGE2 = 2 * kLoadsPerStage;  // loads of two stages
+  constexpr int WAVES = kTileThreads / kWave;
+  __shared__ u32x4_t lds[kTileStages][2][kStageRuns * kRunUnits];
+  // A source rows of this wavefront's two runs (lanes 0..15 run w, 16..31 run w + 8), for
+  // the tiles of even and odd index
+  __shared__ int rows_lds[2][WAVES][kWave];
+  const int NT = (g.NQ + kTilePairs - 1) / kTilePairs;
+  const int n_tiles = *g.n_work * NT;
+  // This workgroup's tiles: XCD x (hardware workgroups are dealt to the 8 XCDs in turn)
+  // owns the x-th contiguous range of logical tiles, and its nbx workgroups take every
+  // nbx-th tile of it, so at any time one XCD works on neighbouring tiles (the row
+  // blocks and column groups of one expert) that share its L2.
+  const int x = blockIdx.x & 7, jx = blockIdx.x >> 3;
+  const int nbx = ((int)gridDim.x - x + 7) >> 3;
+  int start = 0;
+  for (int y = 0; y < x; ++y) start += (n_tiles - y + 7) >> 3;
+  const int cnt = (n_tiles - x + 7) >> 3;
+  const int n_my = jx < cnt ? (cnt - jx + nbx - 1) / nbx : 0;
+  if (n_my == 0) return;  // workgroup-uniform
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int row_units = g.K * 2 / 16;  // 16-byte units per activation row
+  const int NKB = row_units / kChunksPerRow;
+  const int nst = 4 * NKB;             // stages (steps) per tile, a multiple of 4, >= 8
+  const int total = n_my * nst;        // steps of this workgroup
+  const char* Ab = reinterpret_cast<const char*>(g.A);
+  const char* Bb = reinterpret_cast<const char*>(g.B);
+  const uint32_t row_bytes = (uint32_t)row_units * 16u;
+
+  // Tile m of this workgroup: expert, first row, rows, first token, column tile (all
+  // wavefront-uniform).
+  struct TileInfo {
+    int e, row0, M, tok0, nt;
+  };
+  auto info = [&](int m) __attribute__((always_inline)) {
+    const int lt = start + jx + m * nbx;
+    const int item = __builtin_amdgcn_readfirstlane(lt / NT);
+    // the work list is not written while the kernel runs: read it as constant memory
+    // (a scalar load, which the waits for the direct loads do not count)
+    typedef int i32x4_t __attribute__((ext_vector_type(4)));
+    typedef const __attribute__((address_space(4))) i32x4_t* const_work_ptr;
+    const i32x4_t it = ((const_work_ptr)(uintptr_t)g.work)[item];
+    return TileInfo{it[0], it[1], it[2], it[3], lt - item * NT};
+  };
+  // The A source rows of tile t into rows_lds[buf][w]: lane l < 32 holds the row of row
+  // (w + 8*(l/16))*16 + l%16 of the item (rows past its end repeat its last row; their
+  // results go to the sink row). Routed gate/up rows come from row_tok through one 4-byte
+  // direct load (lanes 32..63 repeat lanes 0..31); other rows are consecutive.
+  auto set_rows = [&](const TileInfo& t, int buf) __attribute__((always_inline)) {
+    const int rr = min((w + 8 * ((lane >> 4) & 1)) * 16 + (lane & 15), t.M - 1);
+    if (EPI == EPI_UP && t.e < g.E) {
+      lds_load4(g.row_tok + t.row0 + rr, &rows_lds[buf][w][0]);
+    } else {
+      rows_lds[buf][w][lane] = (EPI == EPI_UP ? t.tok0 : t.row0) + rr;
+    }
+  };
+  // Stage st of tile t (rows src0/src1 of its two A runs): B from the tile's pairs (pairs
+  // past the last repeat it; not stored). Wavefront-uniform base plus a 32-bit per-lane
+  // offset (every operand buffer is below 4 GiB).
+  auto issue = [&](const TileInfo& t, int src0, int src1, int stage) __attribute__((always_inline)) {
+    const int kb = stage >> 2, s = stage & 3, slot = stage & (kTileStages - 1);
+    const uint32_t ka = (uint32_t)(((lane >> 4) + kb * kChunksPerRow + 4 * s) * 16);
+    const int q0 = min(t.nt * kTilePairs + (w >> 1), g.NQ - 1);
+    const int q1 = min(t.nt * kTilePairs + ((w + 8) >> 1), g.NQ - 1);
+    const size_t bk = (size_t)kb * kPairUnits + s * kWave + (w & 1) * 4 * kWave;
+    const size_t b0 = ((size_t)t.e * g.NQ + q0) * (size_t)NKB * kPairUnits + bk;
+    const size_t b1 = ((size_t)t.e * g.NQ + q1) * (size_t)NKB * kPairUnits + bk;
+    const uint32_t lo = (uint32_t)lane * 16u;
+    lds_load16(Ab + ((uint32_t)src0 * row_bytes + ka), &lds[slot][0][w * kRunUnits]);
+    lds_load16(Bb + b0 * 16 + lo, &lds[slot][1][w * kRunUnits]);
+    lds_load16(Ab + ((uint32_t)src1 * row_bytes + ka), &lds[slot][0][(w + 8) * kRunUnits]);
+    lds_load16(Bb + b1 * 16 + lo, &lds[slot][1][(w + 8) * kRunUnits]);
+  };
+
+  const int wm = w >> 2, wn = w & 3;
+  f32x4_t acc[8][2][2];
+  auto clear = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) acc[i][pp][0] = acc[i][pp][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  };
+  // operands of one step (A row tiles 8*wm + i, B tiles (2*wn + pp, t)), two sets
+  u32x4_t fa[2][8], fb[2][2][2];
+  auto read = [&](u32x4_t(&a)[8], u32x4_t(&b)[2][2], int stage) __attribute__((always_inline)) {
+    const int slot = stage & (kTileStages - 1);
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) b[pp][t] = lds[slot][1][((2 * wn + pp) * 2 + t) * kRunUnits + lane];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = lds[slot][0][(8 * wm + i) * kRunUnits + lane];
+  };
+  auto mma = [&](const u32x4_t(&a)[8], const u32x4_t(&b)[2][2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          acc[i][pp][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, b[pp][t]),
+                                                                  __builtin_bit_cast(bf16x8_t, a[i]),
+                                                                  acc[i][pp][t], 0, 0, 0);
+  };
+  // Every lane issues exactly NST stores (rows past the item's end and columns past the
+  // last go to the sink row), so the in-flight counts the waits rely on are exact.
+  auto epilogue = [&](const TileInfo& t) __attribute__((always_inline)) {
+    const int c4 = 4 * (lane >> 4);  // first of the lane's four output columns in a 16-column tile
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 128 * wm + 16 * i + (lane & 15);
+      const bool row_ok = r < t.M;
+      if constexpr (EPI == EPI_UP) {
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+          const int q = t.nt * kTilePairs + 2 * wn + pp;
+          uint32_t v[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) v[j] = f32_to_bf16(swiglu(acc[i][pp][0][j], acc[i][pp][1][j]));
+          const size_t off = row_ok && q < g.NQ ? (size_t)(t.row0 + r) * g.I + stage_ordered_elem(q * 16 + c4)
+                                                : (size_t)g.sink_row * g.I;
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(g.h) + off) =
+              make_uint2(v[0] | (v[1] << 16), v[2] | (v[3] << 16));
+        }
+      } else {
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+          const int q = t.nt * kTilePairs + 2 * wn + pp;
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) {
+            const int col = (2 * q + tt) * 16 + c4;
+            const size_t off = row_ok && q < g.NQ && col < g.H ? (size_t)(t.row0 + r) * g.H + col
+                                                               : (size_t)g.sink_row * g.H;
+            *reinterpret_cast<float4*>(g.ybuf + off) =
+                make_float4(acc[i][pp][tt][0], acc[i][pp][tt][1], acc[i][pp][tt][2], acc[i][pp][tt][3]);
+          }
+        }
+      }
+    }
+  };
+
+  // prologue: tile 0's rows (waited for here), stages 0..2 requested; once stage 0 is in,
+  // stage 3 too, and stage 0 read
+  TileInfo cur = info(0), nxt = cur;
+  if (n_my > 1) nxt = info(1);
+  set_rows(cur, 0);
+  wait_vmem_lds<0>();
+  int src0 = rows_lds[0][w][lane & 15], src1 = rows_lds[0][w][16 + (lane & 15)];
+  clear();
+  issue(cur, src0, src1, 0);
+  issue(cur, src0, src1, 1);
+  issue(cur, src0, src1, 2);
+  wait_vmem_lds<STAGE2>();  // stage 0 in
+  block_barrier();
+  issue(cur, src0, src1, 3);
+  read(fa[0], fb[0], 0);
+
+  // Step gs (tile m, step st of it): wait for this wavefront's loads of stage gs + 1 (the
+  // loads issued after them may stay in flight: two stages, plus the previous tile's
+  // stores in the first three steps of a tile) and for its LDS reads, barrier, read stage
+  // gs + 1's operands and the A rows of the stage to request, multiply stage gs, then
+  // request stage gs + 4 into the slot stage gs freed. The scheduling fences keep that
+  // order (the compiler would otherwise pull each read next to its first use). At step 0
+  // of tile m the rows of tile m + 1 are set (in by step 3, before its first request);
+  // the last step of a tile ends with its epilogue.
+  int m = 0, st = 0;
+  for (int gs = 0; gs < total; gs += 2) {
+    static_for<2>([&](auto sc) __attribute__((always_inline)) {
+      constexpr int u = decltype(sc)::value;
+      const int gcur = gs + u;
+      const bool request = gcur + 4 < total;  // workgroup-uniform
+      const bool own = st + 4 < nst;  // the stage to request is this tile's, else the next's
+      // (the last step reads a stage it does not use: every read stays inside LDS)
+      const int left = total - 2 - gcur;  // stages issued after stage gcur + 1, at most 2
+      if (m > 0 && st < 3) {
+        if constexpr (STAGE2 + NST < 63) wait_vmem_lds<STAGE2 + NST>();
+        else wait_vmem_lds<63>();
+      } else if (left >= 2) {
+        wait_vmem_lds<STAGE2>();
+      } else if (left == 1) {
+        wait_vmem_lds<kLoadsPerStage>();
+      } else {
+        wait_vmem_lds<0>();
+      }
+      block_barrier();
+      read(fa[u ^ 1], fb[u ^ 1], st + 1);
+      const int buf = (m + (own ? 0 : 1)) & 1;
+      const int r0 = rows_lds[buf][w][lane & 15], r1 = rows_lds[buf][w][16 + (lane & 15)];
+      mma(fa[u], fb[u]);
+      // The next stage's 12 LDS reads interleaved with this stage's 32 products (one read
+      // after every two products), so the reads and the address arithmetic fill the
+      // matrix pipe's busy cycles instead of running between the product blocks.
+#pragma unroll
+      for (int i = 0; i < 14; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // two MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      sched_fence();
+      if (request) {
+        if (own) issue(cur, r0, r1, st + 4);
+        else issue(nxt, r0, r1, st + 4 - nst);
+      }
+      if (st == 0 && m + 1 < n_my) set_rows(nxt, (m + 1) & 1);
+      if (++st == nst) {  // workgroup-uniform: tile m done
+        epilogue(cur);
+        clear();
+        st = 0;
+        ++m;
+        cur = nxt;
+        if (m + 1 < n_my) nxt = info(m + 1);
+      }
+    });
+  }
+}
+
+int tiled_tiles_per_item(int NQ) { return (NQ + kTilePairs - 1) / kTilePairs; }
+
+// n_wg: one workgroup per compute unit (each holds 128 KB of LDS); the workgroups walk
+// the tile list themselves.
+hipError_t launch_gemm_tiled(int epi, const GemmArgs& args, unsigned n_wg, hipStream_t stream) {
+  const dim3 grid(n_wg), block(kTileThreads);
+  if (epi == EPI_UP) k_moe_tiled<EPI_UP><<<grid, block, 0, stream>>>(args);
+  else k_moe_tiled<EPI_DOWN><<<grid, block, 0, stream>>>(args);
+  return hipGetLastError();
+}
+
+}  // namespace mv

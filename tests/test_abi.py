@@ -52,6 +52,8 @@ def test_valid_configs_pass(lib):
     assert lib.moe_verify_check_config(ctypes.byref(real)) == bnd.MOE_OK
     for h, wd in ((4096, bnd.MOE_BF16), (2048, bnd.MOE_F32)):  # the largest hidden sizes covered
         assert lib.moe_verify_check_config(ctypes.byref(_cfg(hidden=h, inter=128, wdtype=wd))) == bnd.MOE_OK
+    for h, wd in ((384, bnd.MOE_BF16), (192, bnd.MOE_F32)):  # odd K-block counts are fine without an LM head
+        assert lib.moe_verify_check_config(ctypes.byref(_cfg(hidden=h, inter=128, wdtype=wd, vocab=0))) == bnd.MOE_OK
     assert bnd.last_error() == ""
 
 
@@ -71,6 +73,8 @@ def test_valid_configs_pass(lib):
     (dict(hidden=100), bnd.MOE_EUNSUPPORTED),
     (dict(inter=96), bnd.MOE_EUNSUPPORTED),
     (dict(hidden=192, wdtype=bnd.MOE_BF16), bnd.MOE_EUNSUPPORTED),
+    (dict(hidden=384, inter=128, wdtype=bnd.MOE_BF16), bnd.MOE_EUNSUPPORTED),  # LM head: 256-multiple (bf16)
+    (dict(hidden=192), bnd.MOE_EUNSUPPORTED),  # LM head: 128-multiple (f32)
     (dict(hidden=4224, inter=128, wdtype=bnd.MOE_BF16), bnd.MOE_EUNSUPPORTED),  # above 4096 (bf16)
     (dict(hidden=2112), bnd.MOE_EUNSUPPORTED),                        # above 2048 (f32)
     (dict(max_positions=10_000_000), bnd.MOE_EUNSUPPORTED),

@@ -144,6 +144,50 @@ def test_layer1_bf16_debug_layer_256_positions():
     assert err <= TOL["bf16"]
 
 
+# ----------------------------------------------------------------------------- both expert-GEMM kernels
+
+# A narrow bf16 model without LM head: H = 384 ends the down projection in a partial
+# 256-column tile of the tiled kernel, 16 routed experts top-4 give ragged per-expert
+# row counts, one shared expert, two blocks. Position counts straddle the switch from
+# the streaming expert kernel (fewer than 256 positions) to the tiled one, and 5000
+# positions (20,000 routed slots) take the multi-workgroup routing plan.
+SMALL_BF16 = WL["layer1_bf16"].with_(name="small_bf16", hidden=384, inter=256, n_routed=16, top_k=4, n_shared=1,
+                                     vocab=0, n_layers=2, drafts=0)
+
+
+@pytest.mark.parametrize("T", [255, 256, 300, 1100, 5000])
+def test_small_bf16_both_gemm_paths(T):
+    from gpu_cases import host_weights
+    wl = SMALL_BF16.with_(batch=T)
+    x = W.make_hidden(wl)
+    w = host_weights(wl)
+    ref = O.moe_layer(wl, w, 0, x)
+    m, tid, tw = run_debug_layer(wl, 0, x)
+    dec = ref["gap"] > GATE
+    assert dec.sum() > T // 2
+    np.testing.assert_array_equal(tid[dec], ref["ids"][dec])
+    assert np.abs(tw[dec] - ref["gates"][dec]).max() < 1e-3
+    err = row_rel_err(m[dec], ref["m"][dec])
+    log(f"  layer 0: decisive {dec.sum()}/{T} m rel err {err:.2e}")
+    assert err <= TOL["bf16"]
+    full = O.verify_step(wl, w, x)
+    _, _, hout = run_step(wl, x, T, 0)
+    _check_step(wl, full, None, None, hout, x, min_decisive=T // 4)
+
+
+@pytest.mark.parametrize("B,K", [(75, 3), (300, 0)])
+def test_small_bf16_step_with_lm_head(B, K):
+    """H = 512 with a 1000-token LM head, through the tiled expert kernel (>= 256
+    positions): greedy ids exact on decisive positions, acceptance exact."""
+    from gpu_cases import host_weights
+    wl = SMALL_BF16.with_(name="small_bf16_lm", hidden=512, vocab=1000, batch=B, drafts=K, p_match=0.6)
+    x = W.make_hidden(wl)
+    ref = O.verify_step(wl, host_weights(wl), x)
+    ids, margin, hout = run_step(wl, x, B, K)
+    dec = _check_step(wl, ref, ids, margin, hout, x, min_decisive=wl.positions // 4)
+    _check_accept(wl, ref["ids"], ids, dec)
+
+
 # ----------------------------------------------------------------------------- 12-layer decode
 
 
