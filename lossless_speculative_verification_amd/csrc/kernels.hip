@@ -112,9 +112,9 @@ __device__ __forceinline__ void store4_perm(uint16_t* p, size_t i4, float4 u) {
 //     row 0 in its unused rows, whose results are dropped), float32 accumulation. The
 //     first half of the router weights is requested before step 1, so its latency
 //     overlaps the residual reads.
-//  4. (route, wavefront per position) logit of expert e in lane e plus its bias; k
-//     rounds of a wavefront argmax (larger logit, then lower index) give the selected
-//     experts in slot order; the gates are the softmax of the selected logits.
+//  4. (route, wavefront per position) logit of expert e in lane e plus its bias; the
+//     lane's rank among the 64 (larger logit, then lower index first) is its slot when
+//     below k; the gates are the softmax of the selected logits.
 // Loads never sit behind a branch (the compiler would then wait for every load in
 // flight at the join): indices past the end are clamped and their values masked.
 template <typename T, bool ROUTE, int NP, int VM>
@@ -125,8 +125,12 @@ __global__ __launch_bounds__(256) void k_norm_route(const float* x_in, const flo
                                                     const float* __restrict__ bias,
                                                     int32_t* __restrict__ topk_id, float* __restrict__ topk_w,
                                                     int Tn, int H, int S, int E, int k, float eps, int perm_a) {
-  constexpr int SB = VM <= 5 ? 8 : 4;  // slot rows read together
-  constexpr int RB = 20;               // router K chunks (64 bytes of a row each) per load batch
+  // Batches of loads in flight: slot rows read together and router K chunks (64 bytes of
+  // a row each) per load batch. Small passes (NP = 4) are latency-bound: large batches,
+  // the first router batch requested before anything else. Large passes (NP = 16) are
+  // throughput-bound: batches small enough for three wavefronts per SIMD.
+  constexpr int SB = NP < 16 ? (VM <= 5 ? 8 : 4) : (ROUTE ? 2 : 4);
+  constexpr int RB = NP < 16 ? 20 : 8;
   extern __shared__ uint4 lds_raw[];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int H4 = H >> 2;
@@ -250,30 +254,36 @@ __global__ __launch_bounds__(256) void k_norm_route(const float* x_in, const flo
   for (int p = wave; p < NP; p += kGemmWaves) {
     const int t = blockIdx.x * NP + p;
     if (t >= Tn) continue;
-    float r = lane < E ? r_lds[p * 64 + lane] + bias[lane] : NEG;
+    float* rl = r_lds + p * 64;
+    float r = lane < E ? rl[lane] + bias[lane] : NEG;
     if (r != r) r = NEG;  // a NaN logit ranks last, so every selected id stays below E
-    // Top-k by repeated wavefront argmax; lane j keeps the j-th selection.
-    bool taken = false;
-    float my_v = NEG, v0 = 0.f;
-    int my_e = 0;
-    for (int j = 0; j < k; ++j) {
-      float bv = taken ? NEG : r;
-      int bi = taken ? INT_MAX : lane;
+    // Top-k by rank: lane e's rank is the number of experts ahead of it (a larger logit,
+    // or an equal one at a lower index), i.e. its slot when rank < k. The position's 64
+    // logits are shared through its LDS row (one wavefront per row; LDS operations of a
+    // wavefront complete in order).
+    __builtin_amdgcn_wave_barrier();
+    rl[lane] = r;
+    __builtin_amdgcn_wave_barrier();
+    int rank = 0;
+    float vmax = NEG;
+    const float4* rl4 = reinterpret_cast<const float4*>(rl);
+#pragma unroll 4
+    for (int j4 = 0; j4 < 16; ++j4) {
+      const float4 q = rl4[j4];
+      const float qv[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) {
-        const float ov = __shfl_xor(bv, m, kWave);
-        const int oi = __shfl_xor(bi, m, kWave);
-        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+      for (int c = 0; c < 4; ++c) {
+        const int j = 4 * j4 + c;
+        rank += (qv[c] > r || (qv[c] == r && j < lane)) ? 1 : 0;
+        vmax = fmaxf(vmax, qv[c]);
       }
-      if (lane == bi) taken = true;
-      if (lane == j) { my_v = bv; my_e = bi; }
-      if (j == 0) v0 = bv;
     }
-    const float z = lane < k ? expf(my_v - v0) : 0.f;
+    const bool sel = rank < k;
+    const float z = sel ? expf(r - vmax) : 0.f;  // the softmax over the k selected logits
     const float Z = wave_sum(z);
-    if (lane < k) {
-      topk_id[(size_t)t * k + lane] = my_e;
-      topk_w[(size_t)t * k + lane] = z / Z;
+    if (sel) {
+      topk_id[(size_t)t * k + rank] = lane;
+      topk_w[(size_t)t * k + rank] = z / Z;
     }
   }
 
