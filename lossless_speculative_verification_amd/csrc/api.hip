@@ -229,11 +229,11 @@ int run_block(moe_verify_ctx* c, int l, const float* x_in, const float* ybuf_pre
   // positions are few).
   const int wave_target = c->n_cu * mv::kGemmWaves * MV_GEMM_WAVES_PER_SIMD;
   const int est_items = std::min(E, Tn * k) + S * ((Tn + mb - 1) / mb);
-  auto grid_for = [&](int NQ, int* ppw) -> unsigned {
+  auto grid_for = [&](int NQ, int wpg, int* ppw) -> unsigned {
     if (tiled) return (unsigned)c->n_cu;  // persistent: one workgroup per compute unit
     *ppw = est_items * NQ >= wave_target ? 2 : 1;
     const int chunks = (NQ + *ppw - 1) / *ppw;
-    return (unsigned)((wmax * chunks + mv::kGemmWaves - 1) / mv::kGemmWaves);
+    return (unsigned)((wmax * chunks + wpg - 1) / wpg);
   };
   auto launch = [&](int epi, unsigned n_wg) {
     return tiled ? mv::launch_gemm_tiled(epi, a, n_wg, st) : mv::launch_gemm(g.wdtype, epi, a, n_wg, st);
@@ -245,7 +245,7 @@ int run_block(moe_verify_ctx* c, int l, const float* x_in, const float* ybuf_pre
   a.NQ = c->NQ_up;
   a.h = c->h;
   c->prof_begin(MOE_PROF_GEMM_UP, st);
-  unsigned n_wg = grid_for(c->NQ_up, &a.ppw);
+  unsigned n_wg = grid_for(c->NQ_up, mv::kStreamWavesUp, &a.ppw);
   MV_CHECK(launch(mv::EPI_UP, n_wg));
   c->prof_end(st);
   // down + gate scale
@@ -255,7 +255,7 @@ int run_block(moe_verify_ctx* c, int l, const float* x_in, const float* ybuf_pre
   a.NQ = c->NQ_dn;
   a.ybuf = c->ybuf;
   c->prof_begin(MOE_PROF_GEMM_DOWN, st);
-  n_wg = grid_for(c->NQ_dn, &a.ppw);
+  n_wg = grid_for(c->NQ_dn, mv::kStreamWavesDown, &a.ppw);
   MV_CHECK(launch(mv::EPI_DOWN, n_wg));
   c->prof_end(st);
   return MOE_OK;

@@ -24,8 +24,16 @@ constexpr int kGemmWaves = 4;                       // waves per GEMM workgroup 
 #ifndef MV_GEMM_WAVES_PER_SIMD
 #define MV_GEMM_WAVES_PER_SIMD 2
 #endif
+// Wavefronts per workgroup of the streaming expert GEMM. Each wavefront works alone, and a
+// compute unit's share of the weight stream sets the kernel's time (one CU sustains only
+// so many loads in flight). The gate/up launch has about two workgroups of four per CU;
+// the down launch has fewer chunks per item, and one-wavefront workgroups let the
+// dispatcher spread its wavefronts more evenly over the compute units.
+constexpr int kStreamWavesUp = 4;
+constexpr int kStreamWavesDown = 1;
 constexpr int kGemmMB = 16 * MV_GEMM_NMT;           // rows per expert GEMM work item
 constexpr int kLmRows = 128;                        // positions per LM-head row block
+constexpr int kNormSplitMaxPositions = 4096;  // passes below this use the split norm/router kernel
 constexpr int kTileM = 256;                         // rows per work item of the LDS-tiled expert GEMM
 constexpr int kPlanChunk = 2048;                    // routed slots per workgroup of the large-pass plan
 constexpr int kPlanSingleMaxChunks = 8;             // up to this many chunks one workgroup plans alone

@@ -289,6 +289,230 @@ __global__ __launch_bounds__(256) void k_norm_route(const float* x_in, const flo
 
 }
 
+// Small passes: NP <= 4 positions per workgroup, so the expert-output reads of a pass
+// spread over as many compute units as there are positions (one compute unit streams
+// only so many bytes per microsecond). Eight wavefronts when routing, four otherwise:
+//  * wavefronts 0-3 each own one quarter of the row's float4 columns (VQ per lane). For
+//    each position they read the slot rows and the residual with all loads in flight
+//    together and form x exactly as k_norm_route does (one fused multiply-add per slot in
+//    slot order, then the residual); the sum of squares adds the four quarters' partial
+//    sums in quarter order;
+//  * wavefronts 4-7 (routing) request their 16 experts' router weights, NC chunks of 64
+//    bytes per lane group, as the kernel starts, so those reads overlap the residual
+//    reads; once the normalised rows are in LDS they form the logits with the same
+//    operands as k_norm_route, chunk c accumulating into the fourth (c mod 4) of four
+//    independent MFMA chains that are added at the end;
+//  * wavefront p then selects position p's top-k and gates as in k_norm_route (the bias
+//    is requested as the kernel starts).
+// Workgroup barriers here wait for LDS traffic only: the global stores before them are
+// read by later kernels, never inside this one.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <typename T, bool ROUTE, int NP, int VQ, int NC>
+__global__ __launch_bounds__(ROUTE ? 512 : 256) void k_norm_route_split(const float* x_in, const float* __restrict__ ybuf,
+                                                          const int32_t* __restrict__ slot_row,
+                                                          float* x_out, float* __restrict__ x_copy,
+                                                          T* __restrict__ a_out, const uint4* __restrict__ wr,
+                                                          const float* __restrict__ bias,
+                                                          int32_t* __restrict__ topk_id, float* __restrict__ topk_w,
+                                                          int Tn, int H, int S, int E, int k, float eps, int perm_a) {
+  constexpr int SB = 8;  // slot rows per load batch
+  static_assert(NC % 8 == 0, "router chunks go in groups of eight");
+  extern __shared__ uint4 lds_raw[];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int H4 = H >> 2, Q4 = (H4 + 3) >> 2;
+  const int row_stride = H * (int)sizeof(T) + 16;  // bytes; the pad spreads rows over banks
+  char* a_lds = reinterpret_cast<char*>(lds_raw);
+  float* r_lds = reinterpret_cast<float*>(a_lds + (size_t)NP * row_stride);  // [NP][64] logits
+  float* ss_lds = r_lds + NP * 64;                                              // [NP][4] partial sums
+  const int n64 = H * (int)sizeof(T) / 64;
+  const int t0 = blockIdx.x * NP;
+  // the top-k wavefronts request the router bias now, not after the logits
+  const float bias_l = ROUTE && wave < NP && lane < E ? bias[lane] : 0.f;
+
+  if (ROUTE && wave >= 4) {  // router wavefronts
+    const int e0 = (wave - 4) * 16;
+    const bool route_wave = e0 < E;  // wavefront-uniform
+    const uint4* wp = wr + (size_t)(lane >> 4) * kWave + e0 + (lane & 15);
+    uint4 wbuf[NC];
+#pragma unroll
+    for (int i = 0; i < NC; ++i) wbuf[i] = wp[(size_t)min(i, n64 - 1) * 4 * kWave];
+    lds_barrier();  // sums of squares written
+    lds_barrier();  // normalised rows written
+    if (route_wave) {
+      // chunk c accumulates into acc4[c % 4]: four independent MFMA chains, summed at the end
+      f32x4_t acc4[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc4[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const int row = (lane & 15) < NP ? (lane & 15) : 0;
+      const uint4* arow = reinterpret_cast<const uint4*>(a_lds + (size_t)row * row_stride) + (lane >> 4);
+      const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+      // the prefetched chunks, eight LDS row chunks at a time so the row reads do not all
+      // wait in registers
+      static_for<NC / 8>([&](auto gc) __attribute__((always_inline)) {
+        constexpr int g0 = decltype(gc)::value * 8;
+        uint4 a[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a[i] = arow[min(g0 + i, n64 - 1) * 4];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const bool ok = g0 + i < n64;  // a zero weight chunk adds exactly nothing
+          mma_chunk(acc4[i % 4], a[i], ok ? wbuf[g0 + i] : zero, (T*)nullptr);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      // rows longer than NC chunks (float32 weights, wide rows): the rest eight at a time
+      for (int c0 = NC; c0 < n64; c0 += 8) {
+        uint4 b[8], a[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) b[i] = wp[(size_t)min(c0 + i, n64 - 1) * 4 * kWave];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a[i] = arow[min(c0 + i, n64 - 1) * 4];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) mma_chunk(acc4[i % 4], a[i], c0 + i < n64 ? b[i] : zero, (T*)nullptr);
+      }
+      f32x4_t acc;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = (acc4[0][i] + acc4[1][i]) + (acc4[2][i] + acc4[3][i]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int p = 4 * (lane >> 4) + i;
+        if (p < NP) r_lds[p * 64 + e0 + (lane & 15)] = acc[i];
+      }
+    }
+    lds_barrier();  // logits written
+  } else {
+    const int q0 = wave * Q4;  // this wavefront's first float4 column
+    float4 v[NP][VQ];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int t = t0 + p;
+      float ss = 0.f;
+#pragma unroll
+      for (int j = 0; j < VQ; ++j) v[p][j] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (t < Tn) {  // workgroup-uniform
+        const float4* xi = reinterpret_cast<const float4*>(x_in) + (size_t)t * H4;
+        int col[VQ];
+        bool in[VQ];
+#pragma unroll
+        for (int j = 0; j < VQ; ++j) {
+          const int c = lane + kWave * j;
+          in[j] = c < Q4 && q0 + c < H4;
+          col[j] = in[j] ? q0 + c : 0;
+        }
+        float4 x[VQ];
+#pragma unroll
+        for (int j = 0; j < VQ; ++j) x[j] = xi[col[j]];
+        if (ybuf) {
+          const float4* yb = reinterpret_cast<const float4*>(ybuf);
+          const int KS = k + S;
+          float4 m[VQ];
+#pragma unroll
+          for (int j = 0; j < VQ; ++j) m[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+          for (int s0 = 0; s0 < KS; s0 += SB) {
+            float4 y[SB][VQ];
+            float gt[SB];
+#pragma unroll
+            for (int s = 0; s < SB; ++s) {
+              const int sl = min(s0 + s, KS - 1);  // slot: routed j < k (its gate), then shared (gate 1)
+              const int jr = min(sl, k - 1);
+              const int rr = slot_row[(size_t)t * k + jr];
+              const float gr = topk_w[(size_t)t * k + jr];
+              const size_t row = sl < k ? (size_t)rr : (size_t)Tn * k + (size_t)(sl - k) * Tn + t;
+              gt[s] = sl < k ? gr : 1.0f;
+#pragma unroll
+              for (int j = 0; j < VQ; ++j) y[s][j] = yb[row * H4 + col[j]];
+            }
+#pragma unroll
+            for (int s = 0; s < SB; ++s)
+#pragma unroll
+              for (int j = 0; j < VQ; ++j) {
+                const bool ok = s0 + s < KS;
+                m[j].x = ok ? fmaf(gt[s], y[s][j].x, m[j].x) : m[j].x;
+                m[j].y = ok ? fmaf(gt[s], y[s][j].y, m[j].y) : m[j].y;
+                m[j].z = ok ? fmaf(gt[s], y[s][j].z, m[j].z) : m[j].z;
+                m[j].w = ok ? fmaf(gt[s], y[s][j].w, m[j].w) : m[j].w;
+              }
+          }
+#pragma unroll
+          for (int j = 0; j < VQ; ++j)
+            x[j] = make_float4(x[j].x + m[j].x, x[j].y + m[j].y, x[j].z + m[j].z, x[j].w + m[j].w);
+        }
+#pragma unroll
+        for (int j = 0; j < VQ; ++j) {
+          if (in[j]) {
+            v[p][j] = x[j];
+            if (x_out) reinterpret_cast<float4*>(x_out)[(size_t)t * H4 + col[j]] = x[j];
+            if (x_copy) reinterpret_cast<float4*>(x_copy)[(size_t)t * H4 + col[j]] = x[j];
+            ss += x[j].x * x[j].x + x[j].y * x[j].y + x[j].z * x[j].z + x[j].w * x[j].w;
+          }
+        }
+      }
+      ss = wave_sum(ss);
+      if (lane == 0) ss_lds[p * 4 + wave] = ss;
+    }
+    lds_barrier();  // sums of squares written
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int t = t0 + p;
+      if (t >= Tn) continue;
+      const float ss = ((ss_lds[p * 4] + ss_lds[p * 4 + 1]) + ss_lds[p * 4 + 2]) + ss_lds[p * 4 + 3];
+      const float inv = 1.0f / sqrtf(ss / (float)H + eps);
+      T* lrow = reinterpret_cast<T*>(a_lds + (size_t)p * row_stride);
+#pragma unroll
+      for (int j = 0; j < VQ; ++j) {
+        const int c = lane + kWave * j;
+        if (c < Q4 && q0 + c < H4) {
+          const int i = q0 + c;
+          const float4 u = make_float4(v[p][j].x * inv, v[p][j].y * inv, v[p][j].z * inv, v[p][j].w * inv);
+          if (a_out) {
+            if (perm_a) store4_perm(a_out + (size_t)t * H, i, u);
+            else store4(a_out + (size_t)t * H, i, u);
+          }
+          if (ROUTE) store4(lrow, i, u);
+        }
+      }
+    }
+    if (ROUTE) {
+      lds_barrier();  // normalised rows written
+      lds_barrier();  // logits written
+    }
+  }
+  if (!ROUTE || wave >= NP) return;
+
+  // wavefront p: top-k of position p, as in k_norm_route
+  const int p = wave, t = t0 + p;
+  if (t >= Tn) return;
+  const float NEG = -__builtin_huge_valf();
+  float* rl = r_lds + p * 64;
+  float r = lane < E ? rl[lane] + bias_l : NEG;
+  if (r != r) r = NEG;
+  __builtin_amdgcn_wave_barrier();
+  rl[lane] = r;
+  __builtin_amdgcn_wave_barrier();
+  int rank = 0;
+  float vmax = NEG;
+  const float4* rl4 = reinterpret_cast<const float4*>(rl);
+#pragma unroll 4
+  for (int j4 = 0; j4 < 16; ++j4) {
+    const float4 q = rl4[j4];
+    const float qv[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int j = 4 * j4 + c;
+      rank += (qv[c] > r || (qv[c] == r && j < lane)) ? 1 : 0;
+      vmax = fmaxf(vmax, qv[c]);
+    }
+  }
+  const bool sel = rank < k;
+  const float z = sel ? expf(r - vmax) : 0.f;
+  const float Z = wave_sum(z);
+  if (sel) {
+    topk_id[(size_t)t * k + rank] = lane;
+    topk_w[(size_t)t * k + rank] = z / Z;
+  }
+}
+
 // ============================================================================ routing plan
 
 // The routing plan orders the T*k routed slots (slot = t*k + j) by expert, stably
@@ -624,13 +848,13 @@ __device__ __forceinline__ void moe_stream(const GemmArgs& g, int e, int row0, i
 // so the chunks of one item, and neighbouring items such as the row blocks of one
 // shared expert, share one L2. Logical wavefront lw takes chunk c = lw % chunks (pairs
 // [c*PPW, c*PPW + PPW)) of item lw / chunks.
-template <typename T, int EPI, int NMT, int D>
-__global__ __launch_bounds__(256, MV_GEMM_WAVES_PER_SIMD) void k_moe_gemm(GemmArgs g) {
+template <typename T, int EPI, int NMT, int D, int WPG>
+__global__ __launch_bounds__(kWave * WPG, MV_GEMM_WAVES_PER_SIMD) void k_moe_gemm(GemmArgs g) {
   const int chunks = (g.NQ + g.ppw - 1) / g.ppw;
   const int n_items = *g.n_work;
-  const int n_wg = (n_items * chunks + kGemmWaves - 1) / kGemmWaves;
+  const int n_wg = (n_items * chunks + WPG - 1) / WPG;
   if ((int)blockIdx.x >= n_wg) return;  // workgroup-uniform
-  const int lw = xcd_logical((int)blockIdx.x, n_wg) * kGemmWaves + (threadIdx.x >> 6);
+  const int lw = xcd_logical((int)blockIdx.x, n_wg) * WPG + (threadIdx.x >> 6);
   const int item = lw / chunks, c = lw - item * chunks;
   if (item >= n_items) return;  // no barrier in this kernel
   const int4 it = g.work[item];
@@ -898,10 +1122,13 @@ hipError_t launch_repack_router(const void* src, void* dst, int L, int E, int ro
   return hipGetLastError();
 }
 
-int norm_positions_per_wg(int Tn) { return Tn >= 4096 ? 16 : 4; }
+int norm_positions_per_wg(int Tn) { return Tn >= kNormSplitMaxPositions ? 16 : norm_split_positions(Tn); }
+
+int norm_split_positions(int Tn) { return Tn <= 512 ? 1 : (Tn <= 1024 ? 2 : 4); }
 
 size_t norm_lds_bytes(int wdtype, int H, int np) {
-  return (size_t)np * (H * (wdtype == 1 ? 2 : 4) + 16) + (size_t)np * 64 * sizeof(float);
+  return (size_t)np * (H * (wdtype == 1 ? 2 : 4) + 16) + (size_t)np * 64 * sizeof(float) +
+         (size_t)np * 4 * sizeof(float);
 }
 
 template <typename T, int NP, int VM>
@@ -921,6 +1148,48 @@ static void norm_route_t(bool route, const float* x_in, const float* ybuf, const
                                                                H, S, E, k, eps, perm_a);
 }
 
+template <typename T, int NP, int VQ>
+static void norm_split_t(bool route, const float* x_in, const float* ybuf, const int32_t* slot_row, float* x_out,
+                         float* x_copy, void* a_out, const uint4* w, const float* bias, int32_t* topk_id,
+                         float* topk_w, int Tn, int H, int S, int E, int k, float eps, int perm_a,
+                         hipStream_t stream) {
+  constexpr int NC = 40;  // router chunks requested at the start: a 1280-wide bf16 row
+  const dim3 grid((Tn + NP - 1) / NP);
+  const int wdtype = sizeof(T) == 2 ? 1 : 0;
+  const size_t lds = norm_lds_bytes(wdtype, H, NP);
+  if (route)
+    k_norm_route_split<T, true, NP, VQ, NC><<<grid, dim3(512), lds, stream>>>(
+        x_in, ybuf, slot_row, x_out, x_copy, static_cast<T*>(a_out), w, bias, topk_id, topk_w, Tn, H, S, E, k, eps,
+        perm_a);
+  else
+    k_norm_route_split<T, false, NP, VQ, NC><<<grid, dim3(256), lds, stream>>>(
+        x_in, ybuf, slot_row, x_out, x_copy, static_cast<T*>(a_out), w, bias, topk_id, topk_w, Tn, H, S, E, k, eps,
+        perm_a);
+}
+
+template <typename T, int NP>
+static void norm_split_np(bool route, const float* x_in, const float* ybuf, const int32_t* slot_row, float* x_out,
+                          float* x_copy, void* a_out, const uint4* w, const float* bias, int32_t* topk_id,
+                          float* topk_w, int Tn, int H, int S, int E, int k, float eps, int perm_a,
+                          hipStream_t stream) {
+  const int q4 = (H / 4 + 3) / 4;            // float4 columns per quarter row
+  const int vq = (q4 + kWave - 1) / kWave;  // float4 per lane of one quarter
+  if (vq <= 1) norm_split_t<T, NP, 1>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, stream);
+  else if (vq == 2) norm_split_t<T, NP, 2>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, stream);
+  else norm_split_t<T, NP, 4>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, stream);
+}
+
+template <typename T>
+static void norm_split(bool route, const float* x_in, const float* ybuf, const int32_t* slot_row, float* x_out,
+                       float* x_copy, void* a_out, const uint4* w, const float* bias, int32_t* topk_id,
+                       float* topk_w, int Tn, int H, int S, int E, int k, float eps, int perm_a,
+                       hipStream_t stream) {
+  const int np = norm_split_positions(Tn);
+  if (np == 1) norm_split_np<T, 1>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, stream);
+  else if (np == 2) norm_split_np<T, 2>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, stream);
+  else norm_split_np<T, 4>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, stream);
+}
+
 template <typename T, int NP>
 static void norm_route_np(bool route, const float* x_in, const float* ybuf, const int32_t* slot_row, float* x_out,
                           float* x_copy, void* a_out, const uint4* w, const float* bias, int32_t* topk_id,
@@ -938,13 +1207,13 @@ hipError_t launch_norm_route(int wdtype, bool route, const float* x_in, const fl
                              const float* bias, int32_t* topk_id, float* topk_w, int Tn, int H, int S, int E,
                              int k, float eps, bool perm_a, hipStream_t stream) {
   const uint4* w = static_cast<const uint4*>(wr);
-  const bool big = norm_positions_per_wg(Tn) == 16;
+  const bool big = Tn >= kNormSplitMaxPositions;
   if (wdtype == 1) {
     if (big) norm_route_np<uint16_t, 16>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, stream);
-    else norm_route_np<uint16_t, 4>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, stream);
+    else norm_split<uint16_t>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, stream);
   } else {
     if (big) norm_route_np<float, 16>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, stream);
-    else norm_route_np<float, 4>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, stream);
+    else norm_split<float>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, stream);
   }
   return hipGetLastError();
 }
@@ -964,10 +1233,12 @@ hipError_t launch_plan(const PlanArgs& pa, hipStream_t stream) {
 
 template <typename T>
 static void gemm_t(int epi, const GemmArgs& args, unsigned n_wg, hipStream_t stream) {
-  const dim3 grid(n_wg), block(256);
-  if (epi == EPI_UP) k_moe_gemm<T, EPI_UP, MV_GEMM_NMT, MV_GEMM_D><<<grid, block, 0, stream>>>(args);
-  else if (epi == EPI_DOWN) k_moe_gemm<T, EPI_DOWN, MV_GEMM_NMT, MV_GEMM_D><<<grid, block, 0, stream>>>(args);
-  else k_lm_head<T><<<grid, block, 0, stream>>>(args);
+  const dim3 grid(n_wg);
+  if (epi == EPI_UP)
+    k_moe_gemm<T, EPI_UP, MV_GEMM_NMT, MV_GEMM_D, kStreamWavesUp><<<grid, dim3(kWave * kStreamWavesUp), 0, stream>>>(args);
+  else if (epi == EPI_DOWN)
+    k_moe_gemm<T, EPI_DOWN, MV_GEMM_NMT, MV_GEMM_D, kStreamWavesDown><<<grid, dim3(kWave * kStreamWavesDown), 0, stream>>>(args);
+  else k_lm_head<T><<<grid, dim3(256), 0, stream>>>(args);
 }
 
 hipError_t launch_gemm(int wdtype, int epi, const GemmArgs& args, unsigned n_wg, hipStream_t stream) {

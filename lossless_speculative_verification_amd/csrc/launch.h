@@ -72,6 +72,7 @@ hipError_t launch_gemm_tiled(int epi, const GemmArgs& args, unsigned n_wg, hipSt
 int tiled_tiles_per_item(int NQ);
 // Positions per workgroup of the norm/router kernel and its dynamic LDS bytes.
 int norm_positions_per_wg(int Tn);
+int norm_split_positions(int Tn);
 size_t norm_lds_bytes(int wdtype, int H, int np);
 hipError_t launch_argmax_reduce(const Top2* part, int n_pg, int Tn, int32_t* argmax, float* margin,
                                 hipStream_t stream);
