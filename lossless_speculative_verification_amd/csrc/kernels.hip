@@ -876,23 +876,23 @@ __global__ __launch_bounds__(kWave * WPG, MV_GEMM_WAVES_PER_SIMD) void k_moe_gem
 // buffered, read one K block ahead in registers) and shared by the 4 wavefronts.
 // Weights stream as in moe_stream, two K blocks in flight; no load in the main loop
 // depends on a branch.
-// After each pair, every row's 32 logits are reduced across the 16 column lanes to
-// (top-1 value, lowest index, top-2 value); lane c then folds into its running records
-// only the rows j*16 + c of its lane group's 4*NMT rows (so a lane keeps NMT/4 records,
-// not 4*NMT). At the end the records are merged across the 4 wavefronts and one record
-// per row and workgroup goes to part.
+// The MFMA computes the transposed tile (weights as the first operand, positions as the
+// second), so lane l holds, for position 16*mt + l%16, the logits of columns
+// 32q + 4*(l/16) + i and 32q + 16 + 4*(l/16) + i (i = 0..3) of pair q. Each lane folds
+// them, in increasing column order, into one running (top-1 value, lowest index, top-2
+// value) record per row tile; only at the end are the records merged across the four
+// lane groups and then across the 4 wavefronts, and one record per position and
+// workgroup goes to part.
 template <typename T, int NMT>
 __device__ __forceinline__ void lm_stream(const GemmArgs& g, int row0, int M, int pg, int ppw,
                                           uint4 (*As)[kLmRows][kChunksPerRow + 1],
                                           Top2 (*red)[kLmRows]) {
   constexpr int MB = NMT * 16;
   constexpr int AL = MB * kChunksPerRow / 256;  // 16-byte A chunks per thread per K block
-  constexpr int NR = (4 * NMT + 15) / 16;       // running records per lane
   static_assert(AL >= 1, "row blocks have at least 16 rows");
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int row_units = g.K * (int)sizeof(T) / 16;
   const int NKB = row_units / kChunksPerRow;
-  const int col = lane & 15, rg = (lane >> 4) * 4;
   const int q0 = (pg * kGemmWaves + wave) * ppw;
   const float NEG = -__builtin_huge_valf();
   const int F = ppw * NKB;
@@ -934,39 +934,39 @@ __device__ __forceinline__ void lm_stream(const GemmArgs& g, int row0, int M, in
   };
 
   f32x4_t acc[NMT][2];
-  Top2 best[NR];
+  Top2 best[NMT];  // running record of position 16*mt + lane%16 over this lane's columns
 #pragma unroll
   for (int mt = 0; mt < NMT; ++mt) acc[mt][0] = acc[mt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int j = 0; j < NR; ++j) best[j] = Top2{NEG, INT_MAX, NEG};
+  for (int mt = 0; mt < NMT; ++mt) best[mt] = Top2{NEG, INT_MAX, NEG};
   auto compute = [&](int buf, const uint4(&b)[8]) __attribute__((always_inline)) {
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt) {
         const uint4 a = As[buf][mt * 16 + (lane & 15)][(lane >> 4) * 4 + s];
-        mma_chunk(acc[mt][0], a, b[s], (T*)nullptr);
-        mma_chunk(acc[mt][1], a, b[4 + s], (T*)nullptr);
+        mma_chunk(acc[mt][0], b[s], a, (T*)nullptr);
+        mma_chunk(acc[mt][1], b[4 + s], a, (T*)nullptr);
       }
   };
   auto fold = [&](int q) __attribute__((always_inline)) {  // fold the finished pair q into the running records
-    const int c0 = 2 * q * 16 + col, c1 = c0 + 16;
-    const bool ok0 = q < g.NQ && c0 < g.n_valid, ok1 = q < g.NQ && c1 < g.n_valid;
+    const int cb = 2 * q * 16 + 4 * (lane >> 4);
 #pragma unroll
-    for (int mt = 0; mt < NMT; ++mt)
+    for (int mt = 0; mt < NMT; ++mt) {
+      Top2 b = best[mt];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float v0 = ok0 ? acc[mt][0][i] : NEG;
-        const float v1 = ok1 ? acc[mt][1][i] : NEG;
-        Top2 rec;  // this lane's two columns (c0 < c1: a tie keeps c0)
-        rec.v1 = fmaxf(v0, v1);
-        rec.i1 = v1 > v0 ? c1 : c0;
-        rec.v2 = fminf(v0, v1);
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int m = 1; m < 16; m <<= 1) rec = top2_merge(rec, top2_shfl_xor(rec, m));
-        const int j = mt * 4 + i;  // record j of this lane group: lane j % 16 keeps it
-        if (j % 16 == col) best[j / 16] = top2_merge(best[j / 16], rec);
-      }
+        for (int i = 0; i < 4; ++i) {  // columns in increasing order: a later equal value never wins
+          const int c = cb + 16 * t + i;
+          const float v = (q < g.NQ && c < g.n_valid) ? acc[mt][t][i] : NEG;
+          const bool gt = v > b.v1;
+          b.v2 = gt ? b.v1 : fmaxf(b.v2, v);
+          b.i1 = gt ? c : b.i1;
+          b.v1 = gt ? v : b.v1;
+        }
+      best[mt] = b;
+    }
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) acc[mt][0] = acc[mt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   };
@@ -1008,11 +1008,13 @@ __device__ __forceinline__ void lm_stream(const GemmArgs& g, int row0, int M, in
     fold(q0 + qi);
   }
 
-  // lane c of lane group g holds, in best[k], row (j/4)*16 + 4g + j%4 for j = 16k + c
+  // merge the four lane groups' records of each position; lanes 0-15 then hold them
 #pragma unroll
-  for (int k = 0; k < NR; ++k) {
-    const int j = 16 * k + col;
-    if (j < 4 * NMT) red[wave][(j / 4) * 16 + rg + (j % 4)] = best[k];
+  for (int mt = 0; mt < NMT; ++mt) {
+    Top2 b = best[mt];
+    b = top2_merge(b, top2_shfl_xor(b, 16));
+    b = top2_merge(b, top2_shfl_xor(b, 32));
+    if (lane < 16) red[wave][mt * 16 + lane] = b;
   }
   __syncthreads();
   if ((int)threadIdx.x < M) {
