@@ -139,6 +139,7 @@ struct moe_verify_ctx {
   float* topk_w = nullptr;
   int32_t* row_tok = nullptr;
   int32_t* slot_row = nullptr;  // routed row of each slot (inverse of the expert-major order)
+  int32_t* row_dst = nullptr;   // position-major ybuf row of each routed row (streaming GEMM path)
   int4* work = nullptr;
   int32_t* n_work = nullptr;
   int32_t* chunk_cnt = nullptr;  // [chunks][64] expert counts per slot chunk (large-pass plan)
@@ -203,6 +204,7 @@ int run_block(moe_verify_ctx* c, int l, const float* x_in, const float* ybuf_pre
   pa.Tn = Tn; pa.k = k; pa.E = E; pa.S = S;
   pa.row_tok = c->row_tok;
   pa.slot_row = c->slot_row;
+  pa.row_dst = c->row_dst;
   pa.work = c->work;
   pa.n_work = c->n_work;
   pa.counts = c->counts + (size_t)l * E;
@@ -211,7 +213,7 @@ int run_block(moe_verify_ctx* c, int l, const float* x_in, const float* ybuf_pre
   c->prof_begin(MOE_PROF_NORM_ROUTE, st);
   MV_CHECK(mv::launch_norm_route(g.wdtype, true, x_in, ybuf_prev, c->slot_row, c->x_ws, nullptr, c->a,
                                  c->router_p + l * c->router_units_per_layer, c->bias_p + (size_t)l * 64, c->topk_id,
-                                 c->topk_w, Tn, H, S, E, k, g.rms_eps, tiled, st));
+                                 c->topk_w, Tn, H, S, E, k, g.rms_eps, tiled, !tiled, st));
   c->prof_end(st);
   c->prof_begin(MOE_PROF_PLAN, st);
   MV_CHECK(mv::launch_plan(pa, st));
@@ -222,6 +224,7 @@ int run_block(moe_verify_ctx* c, int l, const float* x_in, const float* ybuf_pre
   a.Tn = Tn;
   a.k = k; a.E = E; a.KS = KS; a.H = H; a.I = I;
   a.row_tok = c->row_tok;
+  a.row_dst = c->row_dst;
   a.max_items = wmax;
   a.sink_row = g.max_positions * KS;  // the extra row past every real row of h and ybuf
   // Streaming kernel: two pairs per wavefront when the expected items x pairs fill at
@@ -333,6 +336,7 @@ MV_API int moe_verify_init(const moe_verify_config* cfg, const moe_verify_weight
   A(&c->topk_w, P * k * sizeof(float));
   A(&c->row_tok, P * k * sizeof(int32_t));
   A(&c->slot_row, P * k * sizeof(int32_t));
+  A(&c->row_dst, P * k * sizeof(int32_t));
   A(&c->work, wmax * sizeof(int4));
   A(&c->n_work, sizeof(int32_t));
   A(&c->chunk_cnt, (size_t)mv::plan_chunks(g.max_positions, k) * 64 * sizeof(int32_t));
@@ -355,6 +359,8 @@ MV_API int moe_verify_init(const moe_verify_config* cfg, const moe_verify_weight
   if ((he = mv::launch_repack_router(w->router_w, c->router_p, L, E, (int)row_h, st)) != hipSuccess)
     return bail(he, "router repack");
   if ((he = hipMemsetAsync(c->bias_p, 0, (size_t)L * 64 * sizeof(float), st)) != hipSuccess) return bail(he, "bias clear");
+  // a work list that no plan has written yet holds no items
+  if ((he = hipMemsetAsync(c->n_work, 0, sizeof(int32_t), st)) != hipSuccess) return bail(he, "work count clear");
   if (w->router_bias &&
       (he = hipMemcpy2DAsync(c->bias_p, 64 * sizeof(float), w->router_bias, E * sizeof(float), E * sizeof(float), L,
                              hipMemcpyDeviceToDevice, st)) != hipSuccess)
@@ -394,7 +400,7 @@ MV_API int moe_verify_step(moe_verify_ctx* c, const float* hidden_in, int32_t B,
   c->prof_begin(MOE_PROF_NORM_ROUTE, st);
   MV_CHECK(mv::launch_norm_route(g.wdtype, false, c->x_ws, c->ybuf, c->slot_row, nullptr, hidden_out,
                                  g.vocab > 0 ? c->a : nullptr, nullptr, nullptr, nullptr, c->topk_w, Tn, g.hidden,
-                                 g.n_shared, g.n_routed, g.top_k, g.rms_eps, false, st));
+                                 g.n_shared, g.n_routed, g.top_k, g.rms_eps, false, !use_tiled(g, Tn), st));
   c->prof_end(st);
   if (g.vocab > 0) {
     // Workgroups (4 wavefronts, two per CU) cover one row block of up to kLmRows
@@ -447,7 +453,9 @@ MV_API int moe_verify_debug_layer(moe_verify_ctx* c, int32_t layer, const float*
   int rc = run_block(c, layer, x_in, nullptr, T, st);
   if (rc) return rc;
   const int KS = g.top_k + g.n_shared;
-  if (moe_out) MV_CHECK(mv::launch_combine(c->ybuf, c->slot_row, c->topk_w, T, g.hidden, g.top_k, g.n_shared, moe_out, st));
+  if (moe_out)
+    MV_CHECK(mv::launch_combine(c->ybuf, c->slot_row, c->topk_w, T, g.hidden, g.top_k, g.n_shared, !use_tiled(g, T),
+                                moe_out, st));
   const size_t kb = (size_t)T * g.top_k * 4;
   if (topk_id) MV_CHECK(hipMemcpyAsync(topk_id, c->topk_id, kb, hipMemcpyDeviceToDevice, st));
   if (topk_w) MV_CHECK(hipMemcpyAsync(topk_w, c->topk_w, kb, hipMemcpyDeviceToDevice, st));

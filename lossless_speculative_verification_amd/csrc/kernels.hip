@@ -124,7 +124,8 @@ __global__ __launch_bounds__(256) void k_norm_route(const float* x_in, const flo
                                                     T* __restrict__ a_out, const uint4* __restrict__ wr,
                                                     const float* __restrict__ bias,
                                                     int32_t* __restrict__ topk_id, float* __restrict__ topk_w,
-                                                    int Tn, int H, int S, int E, int k, float eps, int perm_a) {
+                                                    int Tn, int H, int S, int E, int k, float eps, int perm_a,
+                                                    int pos_major) {
   // Batches of loads in flight: slot rows read together and router K chunks (64 bytes of
   // a row each) per load batch. Small passes (NP = 4) are latency-bound: large batches,
   // the first router batch requested before anything else. Large passes (NP = 16) are
@@ -167,9 +168,10 @@ __global__ __launch_bounds__(256) void k_norm_route(const float* x_in, const flo
         for (int s = 0; s < SB; ++s) {
           const int sl = min(s0 + s, KS - 1);  // slot: routed j < k (its gate), then shared (gate 1)
           const int jr = min(sl, k - 1);
-          const int rr = slot_row[(size_t)t * k + jr];
+          const int rr = pos_major ? 0 : slot_row[(size_t)t * k + jr];
           const float gr = topk_w[(size_t)t * k + jr];
-          const size_t row = sl < k ? (size_t)rr : (size_t)Tn * k + (size_t)(sl - k) * Tn + t;
+          const size_t row = pos_major ? (size_t)t * KS + sl
+                                       : (sl < k ? (size_t)rr : (size_t)Tn * k + (size_t)(sl - k) * Tn + t);
           gt[s] = sl < k ? gr : 1.0f;
 #pragma unroll
           for (int j = 0; j < VM; ++j) y[s][j] = yb[row * H4 + min(lane + kWave * j, H4 - 1)];
@@ -315,7 +317,8 @@ __global__ __launch_bounds__(ROUTE ? 512 : 256) void k_norm_route_split(const fl
                                                           T* __restrict__ a_out, const uint4* __restrict__ wr,
                                                           const float* __restrict__ bias,
                                                           int32_t* __restrict__ topk_id, float* __restrict__ topk_w,
-                                                          int Tn, int H, int S, int E, int k, float eps, int perm_a) {
+                                                          int Tn, int H, int S, int E, int k, float eps, int perm_a,
+                                                    int pos_major) {
   constexpr int SB = 8;  // slot rows per load batch
   static_assert(NC % 8 == 0, "router chunks go in groups of eight");
   extern __shared__ uint4 lds_raw[];
@@ -416,9 +419,10 @@ __global__ __launch_bounds__(ROUTE ? 512 : 256) void k_norm_route_split(const fl
             for (int s = 0; s < SB; ++s) {
               const int sl = min(s0 + s, KS - 1);  // slot: routed j < k (its gate), then shared (gate 1)
               const int jr = min(sl, k - 1);
-              const int rr = slot_row[(size_t)t * k + jr];
+              const int rr = pos_major ? 0 : slot_row[(size_t)t * k + jr];
               const float gr = topk_w[(size_t)t * k + jr];
-              const size_t row = sl < k ? (size_t)rr : (size_t)Tn * k + (size_t)(sl - k) * Tn + t;
+              const size_t row = pos_major ? (size_t)t * KS + sl
+                                           : (sl < k ? (size_t)rr : (size_t)Tn * k + (size_t)(sl - k) * Tn + t);
               gt[s] = sl < k ? gr : 1.0f;
 #pragma unroll
               for (int j = 0; j < VQ; ++j) y[s][j] = yb[row * H4 + col[j]];
@@ -597,6 +601,7 @@ __device__ void seg_scatter(const PlanArgs& pa, int beg, int end, int (*hist)[64
         const int tok = i / k, j = i - tok * k;
         pa.row_tok[pos] = tok;
         pa.slot_row[i] = pos;
+        pa.row_dst[pos] = tok * (k + pa.S) + j;
         if (rank == cnt - 1) hist[wave][key] = pos + 1;
       }
       __builtin_amdgcn_wave_barrier();
@@ -715,9 +720,9 @@ __global__ __launch_bounds__(256) void k_plan_scatter(PlanArgs pa) {
 // load in flight. The epilogue follows the loop:
 //   UP:   tile t = 0 is the gate projection, t = 1 the up projection of the same 16
 //         intermediate columns; the epilogue forms silu(gate) * up and stores it.
-//   DOWN: the epilogue writes the row's expert output to the same row of ybuf (the gate
-//         is applied where the slots are summed); no two wavefronts write the same
-//         element.
+//   DOWN: the epilogue writes the row's expert output to its slot's position-major row
+//         of ybuf, t*(k+S) + j (the gate is applied where the slots are summed); no two
+//         wavefronts write the same element.
 // There is no LDS and no barrier: wavefronts run free.
 template <typename T, int EPI, int NMT, int PPW, int D>
 __device__ __forceinline__ void moe_stream(const GemmArgs& g, int e, int row0, int M, int tok0, int q0) {
@@ -759,6 +764,14 @@ __device__ __forceinline__ void moe_stream(const GemmArgs& g, int e, int row0, i
     if constexpr (EPI == EPI_UP) src = (e < g.E) ? g.row_tok[row0 + rr] : tok0 + rr;
     else src = row0 + rr;
     ap[mt] = reinterpret_cast<const uint4*>(g.A) + (size_t)src * row_units + (lane >> 4) * 4;
+  }
+  // DOWN: lane l holds the position-major ybuf row of item row l % (16*NMT); routed rows
+  // from the plan, shared expert s's row of position t is t*KS + k + s
+  int dst_row = 0;
+  if constexpr (EPI == EPI_DOWN) {
+    const int r = lane & (16 * NMT - 1);
+    const int rr = r < M ? r : 0;
+    dst_row = e < g.E ? g.row_dst[row0 + rr] : (tok0 + rr) * g.KS + g.k + (e - g.E);
   }
   int ka = 0;  // next K block of activations to load
   auto load_a = [&](uint4(&a)[NMT][4]) __attribute__((always_inline)) {
@@ -831,8 +844,9 @@ __device__ __forceinline__ void moe_stream(const GemmArgs& g, int e, int row0, i
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = mt * 16 + rg + i;
+          const int dr = __shfl(dst_row, r, kWave);
           if (r < M) {
-            float* yrow = g.ybuf + (size_t)(row0 + r) * g.H + (2 * q) * 16 + col;
+            float* yrow = g.ybuf + (size_t)dr * g.H + (2 * q) * 16 + col;
             yrow[0] = acc[p][mt][0][i];
             yrow[16] = acc[p][mt][1][i];
           }
@@ -1055,8 +1069,17 @@ __global__ __launch_bounds__(256) void k_argmax_reduce(const Top2* __restrict__ 
   const int t = blockIdx.x * 4 + wave;
   if (t >= Tn) return;
   const float NEG = -__builtin_huge_valf();
+  constexpr int RB = 8;  // records per lane requested together
   Top2 rec{NEG, INT_MAX, NEG};
-  for (int p = lane; p < n_pg; p += kWave) rec = top2_merge(rec, part[(size_t)t * n_pg + p]);
+  const Top2* row = part + (size_t)t * n_pg;
+  for (int p0 = 0; p0 < n_pg; p0 += RB * kWave) {
+    Top2 r[RB];
+#pragma unroll
+    for (int u = 0; u < RB; ++u) r[u] = row[min(p0 + u * kWave + lane, n_pg - 1)];
+#pragma unroll
+    for (int u = 0; u < RB; ++u)  // past the end: the loaded record would count twice, so it is skipped
+      if (p0 + u * kWave + lane < n_pg) rec = top2_merge(rec, r[u]);
+  }
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) rec = top2_merge(rec, top2_shfl_xor(rec, m));
   if (lane == 0) {
@@ -1078,9 +1101,10 @@ __global__ void k_accept(const int32_t* __restrict__ drafts, const int32_t* __re
   for (int i = 0; i <= K; ++i) committed[(size_t)b * (K + 1) + i] = i <= n ? y[i] : -1;
 }
 
-// m[t] = sum_j ybuf[t][j] in slot order (the block output before the residual add).
+// m[t] = sum_j gate_j * y(t, j) in slot order (the block output before the residual add).
 __global__ void k_combine(const float* __restrict__ ybuf, const int32_t* __restrict__ slot_row,
-                          const float* __restrict__ gate, int Tn, int H, int k, int S, float* __restrict__ m) {
+                          const float* __restrict__ gate, int Tn, int H, int k, int S, int pos_major,
+                          float* __restrict__ m) {
   const int H4 = H >> 2;
   const size_t total = (size_t)Tn * H4;
   for (size_t u = (size_t)blockIdx.x * blockDim.x + threadIdx.x; u < total; u += (size_t)gridDim.x * blockDim.x) {
@@ -1088,7 +1112,8 @@ __global__ void k_combine(const float* __restrict__ ybuf, const int32_t* __restr
     const float4* yb = reinterpret_cast<const float4*>(ybuf);
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int j = 0; j < k + S; ++j) {
-      const size_t row = j < k ? (size_t)slot_row[t * k + j] : (size_t)Tn * k + (size_t)(j - k) * Tn + t;
+      const size_t row = pos_major ? t * (size_t)(k + S) + j
+                                   : (j < k ? (size_t)slot_row[t * k + j] : (size_t)Tn * k + (size_t)(j - k) * Tn + t);
       const float gt = j < k ? gate[t * k + j] : 1.0f;
       const float4 y = yb[row * H4 + i];
       s.x = fmaf(gt, y.x, s.x);
@@ -1136,24 +1161,24 @@ size_t norm_lds_bytes(int wdtype, int H, int np) {
 template <typename T, int NP, int VM>
 static void norm_route_t(bool route, const float* x_in, const float* ybuf, const int32_t* slot_row, float* x_out,
                          float* x_copy, void* a_out, const uint4* w, const float* bias, int32_t* topk_id,
-                         float* topk_w, int Tn, int H, int S, int E, int k, float eps, int perm_a,
+                         float* topk_w, int Tn, int H, int S, int E, int k, float eps, int perm_a, int pos_major,
                          hipStream_t stream) {
   const dim3 grid((Tn + NP - 1) / NP), block(256);
   const int wdtype = sizeof(T) == 2 ? 1 : 0;
   if (route)
     k_norm_route<T, true, NP, VM><<<grid, block, norm_lds_bytes(wdtype, H, NP), stream>>>(
         x_in, ybuf, slot_row, x_out, x_copy, static_cast<T*>(a_out), w, bias, topk_id, topk_w, Tn, H, S, E, k, eps,
-        perm_a);
+        perm_a, pos_major);
   else
     k_norm_route<T, false, NP, VM><<<grid, block, 0, stream>>>(x_in, ybuf, slot_row, x_out, x_copy,
                                                                static_cast<T*>(a_out), w, bias, topk_id, topk_w, Tn,
-                                                               H, S, E, k, eps, perm_a);
+                                                               H, S, E, k, eps, perm_a, pos_major);
 }
 
 template <typename T, int NP, int VQ>
 static void norm_split_t(bool route, const float* x_in, const float* ybuf, const int32_t* slot_row, float* x_out,
                          float* x_copy, void* a_out, const uint4* w, const float* bias, int32_t* topk_id,
-                         float* topk_w, int Tn, int H, int S, int E, int k, float eps, int perm_a,
+                         float* topk_w, int Tn, int H, int S, int E, int k, float eps, int perm_a, int pos_major,
                          hipStream_t stream) {
   constexpr int NC = 40;  // router chunks requested at the start: a 1280-wide bf16 row
   const dim3 grid((Tn + NP - 1) / NP);
@@ -1162,60 +1187,60 @@ static void norm_split_t(bool route, const float* x_in, const float* ybuf, const
   if (route)
     k_norm_route_split<T, true, NP, VQ, NC><<<grid, dim3(512), lds, stream>>>(
         x_in, ybuf, slot_row, x_out, x_copy, static_cast<T*>(a_out), w, bias, topk_id, topk_w, Tn, H, S, E, k, eps,
-        perm_a);
+        perm_a, pos_major);
   else
     k_norm_route_split<T, false, NP, VQ, NC><<<grid, dim3(256), lds, stream>>>(
         x_in, ybuf, slot_row, x_out, x_copy, static_cast<T*>(a_out), w, bias, topk_id, topk_w, Tn, H, S, E, k, eps,
-        perm_a);
+        perm_a, pos_major);
 }
 
 template <typename T, int NP>
 static void norm_split_np(bool route, const float* x_in, const float* ybuf, const int32_t* slot_row, float* x_out,
                           float* x_copy, void* a_out, const uint4* w, const float* bias, int32_t* topk_id,
-                          float* topk_w, int Tn, int H, int S, int E, int k, float eps, int perm_a,
+                          float* topk_w, int Tn, int H, int S, int E, int k, float eps, int perm_a, int pos_major,
                           hipStream_t stream) {
   const int q4 = (H / 4 + 3) / 4;            // float4 columns per quarter row
   const int vq = (q4 + kWave - 1) / kWave;  // float4 per lane of one quarter
-  if (vq <= 1) norm_split_t<T, NP, 1>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, stream);
-  else if (vq == 2) norm_split_t<T, NP, 2>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, stream);
-  else norm_split_t<T, NP, 4>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, stream);
+  if (vq <= 1) norm_split_t<T, NP, 1>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, pos_major, stream);
+  else if (vq == 2) norm_split_t<T, NP, 2>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, pos_major, stream);
+  else norm_split_t<T, NP, 4>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, pos_major, stream);
 }
 
 template <typename T>
 static void norm_split(bool route, const float* x_in, const float* ybuf, const int32_t* slot_row, float* x_out,
                        float* x_copy, void* a_out, const uint4* w, const float* bias, int32_t* topk_id,
-                       float* topk_w, int Tn, int H, int S, int E, int k, float eps, int perm_a,
+                       float* topk_w, int Tn, int H, int S, int E, int k, float eps, int perm_a, int pos_major,
                        hipStream_t stream) {
   const int np = norm_split_positions(Tn);
-  if (np == 1) norm_split_np<T, 1>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, stream);
-  else if (np == 2) norm_split_np<T, 2>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, stream);
-  else norm_split_np<T, 4>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, stream);
+  if (np == 1) norm_split_np<T, 1>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, pos_major, stream);
+  else if (np == 2) norm_split_np<T, 2>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, pos_major, stream);
+  else norm_split_np<T, 4>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, pos_major, stream);
 }
 
 template <typename T, int NP>
 static void norm_route_np(bool route, const float* x_in, const float* ybuf, const int32_t* slot_row, float* x_out,
                           float* x_copy, void* a_out, const uint4* w, const float* bias, int32_t* topk_id,
-                          float* topk_w, int Tn, int H, int S, int E, int k, float eps, int perm_a,
+                          float* topk_w, int Tn, int H, int S, int E, int k, float eps, int perm_a, int pos_major,
                           hipStream_t stream) {
   const int vm = (H / 4 + kWave - 1) / kWave;  // float4 per lane of one row
-  if (vm <= 2) norm_route_t<T, NP, 2>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, stream);
-  else if (vm == 5) norm_route_t<T, NP, 5>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, stream);
-  else if (vm <= 8) norm_route_t<T, NP, 8>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, stream);
-  else norm_route_t<T, NP, 16>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, stream);
+  if (vm <= 2) norm_route_t<T, NP, 2>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, pos_major, stream);
+  else if (vm == 5) norm_route_t<T, NP, 5>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, pos_major, stream);
+  else if (vm <= 8) norm_route_t<T, NP, 8>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, pos_major, stream);
+  else norm_route_t<T, NP, 16>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, pos_major, stream);
 }
 
 hipError_t launch_norm_route(int wdtype, bool route, const float* x_in, const float* ybuf,
                              const int32_t* slot_row, float* x_out, float* x_copy, void* a_out, const void* wr,
                              const float* bias, int32_t* topk_id, float* topk_w, int Tn, int H, int S, int E,
-                             int k, float eps, bool perm_a, hipStream_t stream) {
+                             int k, float eps, bool perm_a, bool pos_major, hipStream_t stream) {
   const uint4* w = static_cast<const uint4*>(wr);
   const bool big = Tn >= kNormSplitMaxPositions;
   if (wdtype == 1) {
-    if (big) norm_route_np<uint16_t, 16>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, stream);
-    else norm_split<uint16_t>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, stream);
+    if (big) norm_route_np<uint16_t, 16>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, pos_major, stream);
+    else norm_split<uint16_t>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, pos_major, stream);
   } else {
-    if (big) norm_route_np<float, 16>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, stream);
-    else norm_split<float>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, stream);
+    if (big) norm_route_np<float, 16>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, pos_major, stream);
+    else norm_split<float>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, pos_major, stream);
   }
   return hipGetLastError();
 }
@@ -1262,8 +1287,9 @@ hipError_t launch_accept(const int32_t* drafts, const int32_t* argmax, int B, in
 }
 
 hipError_t launch_combine(const float* ybuf, const int32_t* slot_row, const float* gate, int Tn, int H, int k,
-                          int S, float* m, hipStream_t stream) {
-  k_combine<<<grid_for((size_t)Tn * (H / 4), 256), 256, 0, stream>>>(ybuf, slot_row, gate, Tn, H, k, S, m);
+                          int S, bool pos_major, float* m, hipStream_t stream) {
+  k_combine<<<grid_for((size_t)Tn * (H / 4), 256), 256, 0, stream>>>(ybuf, slot_row, gate, Tn, H, k, S,
+                                                                      pos_major ? 1 : 0, m);
   return hipGetLastError();
 }
 

@@ -17,6 +17,7 @@ struct PlanArgs {
   int Tn, k, E, S;
   int32_t* row_tok;   // out: token of each routed row
   int32_t* slot_row;  // out: routed row of each slot t*k + j
+  int32_t* row_dst;   // out: position-major ybuf row t*(k+S) + j of each routed row
   int4* work;
   int32_t* n_work;
   int32_t* counts;
@@ -30,6 +31,7 @@ struct GemmArgs {
   const int32_t* n_work;   // number of valid work items (device)
   const void* A;           // activation rows: UP a[T][H] (gathered), DOWN h[rows][I], LM a[T][H]
   const int32_t* row_tok;  // UP: token of each routed row
+  const int32_t* row_dst;  // streaming DOWN: position-major ybuf row of each routed row
   const uint4* B;          // packed weights of this layer (pair layout)
   int K;                   // contraction length in elements
   int NQ;                  // column pairs (2 x 16 columns) per expert
@@ -51,13 +53,14 @@ hipError_t launch_repack_pairs(const void* src0, const void* src1, void* dst, in
                                hipStream_t stream);
 hipError_t launch_repack_router(const void* src, void* dst, int L, int E, int row_bytes,
                                 hipStream_t stream);
-// Combine of the previous block (ybuf rows gathered through slot_row, gates from topk_w)
-// + residual + RMSNorm (+ router and top-k when route, overwriting topk_id/topk_w);
-// a_out in the stage-ordered row layout when perm_a (bf16 only).
+// Combine of the previous block (gates from topk_w; ybuf rows position-major, t*(k+S) + j,
+// when pos_major, else gathered through slot_row) + residual + RMSNorm (+ router and
+// top-k when route, overwriting topk_id/topk_w); a_out in the stage-ordered row layout
+// when perm_a (bf16 only).
 hipError_t launch_norm_route(int wdtype, bool route, const float* x_in, const float* ybuf,
                              const int32_t* slot_row, float* x_out, float* x_copy, void* a_out, const void* wr,
                              const float* bias, int32_t* topk_id, float* topk_w, int Tn, int H, int S, int E,
-                             int k, float eps, bool perm_a, hipStream_t stream);
+                             int k, float eps, bool perm_a, bool pos_major, hipStream_t stream);
 // Routing plan: one workgroup for up to kPlanSingleMaxChunks chunks of kPlanChunk slots
 // (or when chunk_cnt is NULL), else a count pass and a scatter pass of one workgroup
 // per chunk.
@@ -78,8 +81,9 @@ hipError_t launch_argmax_reduce(const Top2* part, int n_pg, int Tn, int32_t* arg
                                 hipStream_t stream);
 hipError_t launch_accept(const int32_t* drafts, const int32_t* argmax, int B, int K, int32_t* accepted,
                          int32_t* committed, hipStream_t stream);
-// m[t] = sum_j gate[t][j] * ybuf[slot_row[t*k + j]] + sum_s ybuf[T*k + s*T + t].
+// m[t] = sum_j gate[t][j] * y(t, j) + sum_s y(t, k + s), with y(t, j) = ybuf[t*(k+S) + j]
+// when pos_major, else ybuf[slot_row[t*k + j]] (j < k) and ybuf[T*k + s*T + t] (shared).
 hipError_t launch_combine(const float* ybuf, const int32_t* slot_row, const float* gate, int Tn, int H, int k,
-                          int S, float* m, hipStream_t stream);
+                          int S, bool pos_major, float* m, hipStream_t stream);
 
 }  // namespace mv
