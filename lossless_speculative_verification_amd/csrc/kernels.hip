@@ -1211,7 +1211,7 @@ static void norm_split(bool route, const float* x_in, const float* ybuf, const i
                        float* x_copy, void* a_out, const uint4* w, const float* bias, int32_t* topk_id,
                        float* topk_w, int Tn, int H, int S, int E, int k, float eps, int perm_a, int pos_major,
                        hipStream_t stream) {
-  const int np = norm_split_positions(Tn);
+  const int np = route ? norm_split_positions(Tn) : 1;  // no router weights to share: one position per workgroup
   if (np == 1) norm_split_np<T, 1>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, pos_major, stream);
   else if (np == 2) norm_split_np<T, 2>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, pos_major, stream);
   else norm_split_np<T, 4>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, pos_major, stream);
@@ -1234,7 +1234,8 @@ hipError_t launch_norm_route(int wdtype, bool route, const float* x_in, const fl
                              const float* bias, int32_t* topk_id, float* topk_w, int Tn, int H, int S, int E,
                              int k, float eps, bool perm_a, bool pos_major, hipStream_t stream) {
   const uint4* w = static_cast<const uint4*>(wr);
-  const bool big = Tn >= kNormSplitMaxPositions;
+  // the no-router combine (the final norm) runs split at every size
+  const bool big = route && Tn >= kNormSplitMaxPositions;
   if (wdtype == 1) {
     if (big) norm_route_np<uint16_t, 16>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, pos_major, stream);
     else norm_split<uint16_t>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, pos_major, stream);
