@@ -191,8 +191,10 @@ namespace {
   } while (0)
 
 // Launch the MoE block `l` over Tn positions whose residual input is x_in (plus the
-// previous block's ybuf when given). Leaves the block's per-slot outputs in ybuf.
-int run_block(moe_verify_ctx* c, int l, const float* x_in, const float* ybuf_prev, int Tn, hipStream_t st) {
+// previous block's ybuf when given; that sum is stored to x_out when given, which may be
+// x_in itself). Leaves the block's per-slot outputs in ybuf.
+int run_block(moe_verify_ctx* c, int l, const float* x_in, const float* ybuf_prev, float* x_out, int Tn,
+              hipStream_t st) {
   const moe_verify_config& g = c->cfg;
   const int E = g.n_routed, S = g.n_shared, k = g.top_k, KS = k + S, H = g.hidden, I = g.inter;
   const bool tiled = use_tiled(g, Tn);
@@ -211,7 +213,7 @@ int run_block(moe_verify_ctx* c, int l, const float* x_in, const float* ybuf_pre
   pa.mb = mb;
   pa.chunk_cnt = c->chunk_cnt;
   c->prof_begin(MOE_PROF_NORM_ROUTE, st);
-  MV_CHECK(mv::launch_norm_route(g.wdtype, true, x_in, ybuf_prev, c->slot_row, c->x_ws, nullptr, c->a,
+  MV_CHECK(mv::launch_norm_route(g.wdtype, true, x_in, ybuf_prev, c->slot_row, x_out, nullptr, c->a,
                                  c->router_p + l * c->router_units_per_layer, c->bias_p + (size_t)l * 64, c->topk_id,
                                  c->topk_w, Tn, H, S, E, k, g.rms_eps, tiled, !tiled, st));
   c->prof_end(st);
@@ -393,12 +395,13 @@ MV_API int moe_verify_step(moe_verify_ctx* c, const float* hidden_in, int32_t B,
   if (dg.err != hipSuccess) return fail(MOE_EDEVICE, "device select: %s", hipGetErrorString(dg.err));
   c->n_pairs = 0;
   for (int l = 0; l < g.n_layers; ++l) {
-    rc = run_block(c, l, l == 0 ? hidden_in : c->x_ws, l == 0 ? nullptr : c->ybuf, Tn, st);
+    // block 0's residual is hidden_in itself: block 1 reads it there, so it is not copied
+    rc = run_block(c, l, l <= 1 ? hidden_in : c->x_ws, l == 0 ? nullptr : c->ybuf, l == 0 ? nullptr : c->x_ws, Tn, st);
     if (rc) return rc;
   }
   const int KS = g.top_k + g.n_shared;
   c->prof_begin(MOE_PROF_NORM_ROUTE, st);
-  MV_CHECK(mv::launch_norm_route(g.wdtype, false, c->x_ws, c->ybuf, c->slot_row, nullptr, hidden_out,
+  MV_CHECK(mv::launch_norm_route(g.wdtype, false, g.n_layers == 1 ? hidden_in : c->x_ws, c->ybuf, c->slot_row, nullptr, hidden_out,
                                  g.vocab > 0 ? c->a : nullptr, nullptr, nullptr, nullptr, c->topk_w, Tn, g.hidden,
                                  g.n_shared, g.n_routed, g.top_k, g.rms_eps, false, !use_tiled(g, Tn), st));
   c->prof_end(st);
@@ -450,7 +453,7 @@ MV_API int moe_verify_debug_layer(moe_verify_ctx* c, int32_t layer, const float*
   hipStream_t st = static_cast<hipStream_t>(stream);
   DeviceGuard dg(c->device);
   if (dg.err != hipSuccess) return fail(MOE_EDEVICE, "device select: %s", hipGetErrorString(dg.err));
-  int rc = run_block(c, layer, x_in, nullptr, T, st);
+  int rc = run_block(c, layer, x_in, nullptr, nullptr, T, st);
   if (rc) return rc;
   const int KS = g.top_k + g.n_shared;
   if (moe_out)
