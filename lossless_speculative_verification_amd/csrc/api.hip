@@ -217,9 +217,13 @@ int run_block(moe_verify_ctx* c, int l, const float* x_in, const float* ybuf_pre
                                  c->router_p + l * c->router_units_per_layer, c->bias_p + (size_t)l * 64, c->topk_id,
                                  c->topk_w, Tn, H, S, E, k, g.rms_eps, tiled, !tiled, st));
   c->prof_end(st);
-  c->prof_begin(MOE_PROF_PLAN, st);
-  MV_CHECK(mv::launch_plan(pa, st));
-  c->prof_end(st);
+  // small streaming passes: the gate/up GEMM builds the plan in its prologue
+  const bool self_plan = !tiled && Tn * k <= mv::kSelfPlanMaxSlots;
+  if (!self_plan) {
+    c->prof_begin(MOE_PROF_PLAN, st);
+    MV_CHECK(mv::launch_plan(pa, st));
+    c->prof_end(st);
+  }
   mv::GemmArgs a{};
   a.work = c->work;
   a.n_work = c->n_work;
@@ -229,6 +233,12 @@ int run_block(moe_verify_ctx* c, int l, const float* x_in, const float* ybuf_pre
   a.row_dst = c->row_dst;
   a.max_items = wmax;
   a.sink_row = g.max_positions * KS;  // the extra row past every real row of h and ybuf
+  a.topk_id = c->topk_id;
+  a.plan_work = c->work;
+  a.plan_n_work = c->n_work;
+  a.plan_counts = pa.counts;
+  a.plan_row_dst = c->row_dst;
+  a.mb = mb;
   // Streaming kernel: two pairs per wavefront when the expected items x pairs fill at
   // least one round of resident wavefronts (routed items: one per touched expert while
   // positions are few).
@@ -251,7 +261,8 @@ int run_block(moe_verify_ctx* c, int l, const float* x_in, const float* ybuf_pre
   a.h = c->h;
   c->prof_begin(MOE_PROF_GEMM_UP, st);
   unsigned n_wg = grid_for(c->NQ_up, mv::kStreamWavesUp, &a.ppw);
-  MV_CHECK(launch(mv::EPI_UP, n_wg));
+  if (self_plan) MV_CHECK(mv::launch_gemm_planned(g.wdtype, a, n_wg, st));
+  else MV_CHECK(launch(mv::EPI_UP, n_wg));
   c->prof_end(st);
   // down + gate scale
   a.A = c->h;

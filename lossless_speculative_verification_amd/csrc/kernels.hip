@@ -725,7 +725,8 @@ __global__ __launch_bounds__(256) void k_plan_scatter(PlanArgs pa) {
 //         wavefronts write the same element.
 // There is no LDS and no barrier: wavefronts run free.
 template <typename T, int EPI, int NMT, int PPW, int D>
-__device__ __forceinline__ void moe_stream(const GemmArgs& g, int e, int row0, int M, int tok0, int q0) {
+__device__ __forceinline__ void moe_stream(const GemmArgs& g, int e, int row0, int M, int tok0, int q0,
+                                           const int* tok_lds = nullptr) {
   const int lane = threadIdx.x & 63;
   const int row_units = g.K * (int)sizeof(T) / 16;
   const int NKB = row_units / kChunksPerRow;
@@ -761,7 +762,7 @@ __device__ __forceinline__ void moe_stream(const GemmArgs& g, int e, int row0, i
     const int r = mt * 16 + (lane & 15);
     const int rr = r < M ? r : 0;
     int src;
-    if constexpr (EPI == EPI_UP) src = (e < g.E) ? g.row_tok[row0 + rr] : tok0 + rr;
+    if constexpr (EPI == EPI_UP) src = (e < g.E) ? (tok_lds ? tok_lds[rr] : g.row_tok[row0 + rr]) : tok0 + rr;
     else src = row0 + rr;
     ap[mt] = reinterpret_cast<const uint4*>(g.A) + (size_t)src * row_units + (lane >> 4) * 4;
   }
@@ -880,6 +881,115 @@ __global__ __launch_bounds__(kWave * WPG, MV_GEMM_WAVES_PER_SIMD) void k_moe_gem
   } else {
     if (one_tile) moe_stream<T, EPI, 1, 1, D + 1>(g, it.x, it.y, it.z, it.w, q0);
     else moe_stream<T, EPI, NMT, 1, D + 1>(g, it.x, it.y, it.z, it.w, q0);
+  }
+}
+
+// Gate/up expert GEMM of the streaming path that builds the routing plan itself, so that
+// no plan kernel runs between the norm/router kernel and this one. Every workgroup
+// computes the same plan from the N = T*k routed ids (at most kSelfPlanMaxSlots):
+// per-expert counts by LDS histogram, then, in wavefront 0, the items per expert
+// (ceil(count / mb)) and the expert's first row, by lane scans; the item order, row space
+// and row order are those of k_plan (shared experts' position blocks first, then the
+// routed experts' row blocks in expert order; an expert's slots in ascending slot order).
+// A wavefront then finds its item as in k_moe_gemm, compacts its expert's slots of rank
+// [b*mb, b*mb + M) with ballots into LDS (tokens for the activation rows, slot ids for
+// row_dst), and runs moe_stream. The item's chunk-0 wavefront writes the work item and the
+// rows' position-major ybuf rows for the down GEMM; workgroup 0 writes the item count and
+// the per-expert counts.
+template <typename T, int NMT, int D, int WPG>
+__global__ __launch_bounds__(kWave * WPG, MV_GEMM_WAVES_PER_SIMD) void k_moe_gemm_planned(GemmArgs g) {
+  __shared__ int ids[kSelfPlanMaxSlots];
+  __shared__ int hist[kWave];
+  __shared__ int first_item[kWave + 1];  // routed expert e's items start at first_item[e]
+  __shared__ int first_row[kWave];       // and its rows at first_row[e]
+  __shared__ int rows[WPG][2][16 * NMT];  // per wavefront: tokens and slots of its item's rows
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int N = g.Tn * g.k, E = g.E, mb = g.mb;
+  const int S = g.KS - g.k;
+  const int mbT = (g.Tn + mb - 1) / mb, nsw = S * mbT;  // shared-expert items come first
+  for (int i = threadIdx.x; i < kWave; i += blockDim.x) hist[i] = 0;
+  __syncthreads();
+  for (int i0 = 0; i0 < N; i0 += 4 * (int)blockDim.x) {
+    int id[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) id[u] = g.topk_id[min(i0 + u * (int)blockDim.x + (int)threadIdx.x, N - 1)];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * (int)blockDim.x + (int)threadIdx.x;
+      if (i < N) {
+        const int e = min(max(id[u], 0), E - 1);  // ids come from the router, always < E
+        ids[i] = e;
+        atomicAdd(&hist[e], 1);
+      }
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const int c = lane < E ? hist[lane] : 0;
+    const int nb = (c + mb - 1) / mb;
+    int sc = c, sn = nb;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int oc = __shfl_up(sc, d, kWave), on = __shfl_up(sn, d, kWave);
+      if (lane >= d) { sc += oc; sn += on; }
+    }
+    first_row[lane] = sc - c;
+    first_item[lane] = nsw + sn - nb;
+    if (lane == kWave - 1) first_item[kWave] = nsw + sn;
+    if (blockIdx.x == 0 && lane < E) g.plan_counts[lane] = c;
+  }
+  __syncthreads();
+  const int n_items = first_item[kWave];
+  if (blockIdx.x == 0 && threadIdx.x == 0) *g.plan_n_work = n_items;
+  const int chunks = (g.NQ + g.ppw - 1) / g.ppw;
+  const int n_wg = (n_items * chunks + WPG - 1) / WPG;
+  if ((int)blockIdx.x >= n_wg) return;  // workgroup-uniform
+  const int lw = xcd_logical((int)blockIdx.x, n_wg) * WPG + wave;
+  const int item = lw / chunks, c = lw - item * chunks;
+  if (item >= n_items) return;  // no barrier from here on
+  int e, row0, M, tok0;
+  int* tok_rows = rows[wave][0];
+  int* slot_rows = rows[wave][1];
+  if (item < nsw) {
+    const int s = item / mbT, b = item - s * mbT;
+    e = E + s; row0 = N + s * g.Tn + b * mb; M = min(mb, g.Tn - b * mb); tok0 = b * mb;
+  } else {
+    // the routed expert whose items contain this one: the last e with first_item[e] <= item
+    const unsigned long long le = __ballot(lane < E && first_item[lane] <= item);
+    e = 63 - __clzll(le);
+    const int b = item - first_item[e];
+    const int cnt = hist[e];
+    row0 = first_row[e] + b * mb; M = min(mb, cnt - b * mb); tok0 = 0;
+    // the expert's slots of rank [b*mb, b*mb + M), 64 ids at a time, in slot order
+    int base = 0;
+    for (int i0 = 0; i0 < N && base < b * mb + M; i0 += kWave) {  // wavefront-uniform
+      const int i = i0 + lane;
+      const bool hit = i < N && ids[i] == e;
+      const unsigned long long m = __ballot(hit);
+      const int r = base + __popcll(m & ((1ull << lane) - 1ull)) - b * mb;
+      if (hit && r >= 0 && r < M) {
+        tok_rows[r] = i / g.k;
+        slot_rows[r] = i;
+      }
+      base += __popcll(m);
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+  if (c == 0) {  // the item's first chunk publishes it for the down GEMM
+    if (lane == 0) g.plan_work[item] = make_int4(e, row0, M, tok0);
+    if (e < E && lane < M) {
+      const int i = slot_rows[lane];
+      g.plan_row_dst[row0 + lane] = (i / g.k) * g.KS + (i - (i / g.k) * g.k);
+    }
+  }
+  const int q0 = c * g.ppw;
+  const bool one_tile = NMT > 1 && M <= 16;
+  if (g.ppw == 2) {
+    if (one_tile) moe_stream<T, EPI_UP, 1, 2, D>(g, e, row0, M, tok0, q0, tok_rows);
+    else moe_stream<T, EPI_UP, NMT, 2, D>(g, e, row0, M, tok0, q0, tok_rows);
+  } else {
+    if (one_tile) moe_stream<T, EPI_UP, 1, 1, D + 1>(g, e, row0, M, tok0, q0, tok_rows);
+    else moe_stream<T, EPI_UP, NMT, 1, D + 1>(g, e, row0, M, tok0, q0, tok_rows);
   }
 }
 
@@ -1267,6 +1377,15 @@ static void gemm_t(int epi, const GemmArgs& args, unsigned n_wg, hipStream_t str
   else if (epi == EPI_DOWN)
     k_moe_gemm<T, EPI_DOWN, MV_GEMM_NMT, MV_GEMM_D, kStreamWavesDown><<<grid, dim3(kWave * kStreamWavesDown), 0, stream>>>(args);
   else k_lm_head<T><<<grid, dim3(256), 0, stream>>>(args);
+}
+
+hipError_t launch_gemm_planned(int wdtype, const GemmArgs& args, unsigned n_wg, hipStream_t stream) {
+  const dim3 grid(n_wg), block(kWave * kStreamWavesUp);
+  if (wdtype == 1)
+    k_moe_gemm_planned<uint16_t, MV_GEMM_NMT, MV_GEMM_D, kStreamWavesUp><<<grid, block, 0, stream>>>(args);
+  else
+    k_moe_gemm_planned<float, MV_GEMM_NMT, MV_GEMM_D, kStreamWavesUp><<<grid, block, 0, stream>>>(args);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm(int wdtype, int epi, const GemmArgs& args, unsigned n_wg, hipStream_t stream) {

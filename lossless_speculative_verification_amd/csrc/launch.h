@@ -46,6 +46,15 @@ struct GemmArgs {
   int ppw;                 // expert GEMMs: column pairs per wavefront (1 or 2)
   int max_items;           // expert GEMMs: capacity of the work list (grid covers max_items x chunks)
   int sink_row;            // tiled expert GEMMs: row of h / ybuf that takes the stores of padding rows
+  // Streaming gate/up that builds the routing plan itself (launch_gemm_planned): it reads
+  // topk_id and writes the work list, item count, per-expert counts and row_dst that the
+  // plan kernel would have written (for the down GEMM and the bench), with items of mb rows.
+  const int32_t* topk_id;
+  int4* plan_work;
+  int32_t* plan_n_work;
+  int32_t* plan_counts;
+  int32_t* plan_row_dst;
+  int mb;
 };
 
 hipError_t launch_repack_pairs(const void* src0, const void* src1, void* dst, int n_mats, int N,
@@ -68,6 +77,9 @@ hipError_t launch_plan(const PlanArgs& pa, hipStream_t stream);
 int plan_chunks(int Tn, int k);
 // One-dimensional grid of n_wg workgroups (item x column-pair group, see k_gemm).
 hipError_t launch_gemm(int wdtype, int epi, const GemmArgs& args, unsigned n_wg, hipStream_t stream);
+// Gate/up of the streaming path with the plan built in its prologue (no launch_plan), for
+// passes of at most kSelfPlanMaxSlots routed slots; same grid as launch_gemm(EPI_UP).
+hipError_t launch_gemm_planned(int wdtype, const GemmArgs& args, unsigned n_wg, hipStream_t stream);
 // LDS-tiled expert GEMM (bf16) over work items of up to kTileM rows and
 // tiled_tiles_per_item(NQ) column tiles each; n_wg persistent workgroups (one per compute
 // unit) share the tiles. Needs K >= 256 elements.
