@@ -25,6 +25,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA peak
 TILED_MIN_POSITIONS = 256       # the library's switch to the tiled expert GEMM (bf16)
+SELF_PLAN_MAX_SLOTS = 4096      # the library's limit for the plan built inside the streaming gate/up GEMM
 
 METRIC = "verified tokens/sec per verify step (B=32,K=3,12 layers); % HBM roofline"
 
@@ -204,7 +205,11 @@ def main():
     # least TILED_MIN_POSITIONS positions (matrix-core bound there), else on the streaming
     # kernel (bound by the weight stream).
     tiled = wl.wdtype == "bf16" and T >= TILED_MIN_POSITIONS
-    kernel = "k_moe_tiled<0>" if tiled else "k_moe_gemm<bf16,0"
+    # streaming passes of at most SELF_PLAN_MAX_SLOTS routed slots build the plan inside
+    # the gate/up kernel (k_moe_gemm_planned)
+    planned = not tiled and T * wl.top_k <= SELF_PLAN_MAX_SLOTS
+    dt = "bf16" if wl.wdtype == "bf16" else "float"
+    kernel = "k_moe_tiled<0>" if tiled else (f"k_moe_gemm_planned<{dt}" if planned else f"k_moe_gemm<{dt},0")
     # measured HBM bytes per launch of the same kernel (rocprofv3 counters, see profiles/),
     # only while the counters were taken on the current kernel sources
     from lossless_speculative_verification_amd import profiling
@@ -220,7 +225,8 @@ def main():
                 "frac": round(up_tfs / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic_up,
                 "algorithmic_flops_per_launch": acc["up_flops_per_launch"], "avg_launch_us": round(up_us, 2)}
     else:
-        roof = {"bound": "hbm", "kernel": "gate/up expert GEMM + SwiGLU (k_moe_gemm, one launch per block)",
+        roof = {"bound": "hbm", "kernel": "gate/up expert GEMM + SwiGLU (%s, one launch per block)"
+                                          % ("k_moe_gemm_planned" if planned else "k_moe_gemm"),
                 "achieved": round(up_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(up_gbs / HBM_PEAK_GBS, 4), "traffic": traffic_up,
                 "algorithmic_bytes_per_launch": round(acc["up_bytes_per_launch"]), "avg_launch_us": round(up_us, 2)}
