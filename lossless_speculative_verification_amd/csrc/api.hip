@@ -144,7 +144,7 @@ struct moe_verify_ctx {
   int32_t* n_work = nullptr;
   int32_t* chunk_cnt = nullptr;  // [chunks][64] expert counts per slot chunk (large-pass plan)
   void* h = nullptr;
-  float* ybuf = nullptr;
+  void* ybuf = nullptr;  // expert outputs, one row per slot, in the weight element type
   mv::Top2* part = nullptr;
   int32_t* counts = nullptr;  // [L][E] routed-slot count per expert, last step
   std::vector<void*> allocs;
@@ -193,7 +193,7 @@ namespace {
 // Launch the MoE block `l` over Tn positions whose residual input is x_in (plus the
 // previous block's ybuf when given; that sum is stored to x_out when given, which may be
 // x_in itself). Leaves the block's per-slot outputs in ybuf.
-int run_block(moe_verify_ctx* c, int l, const float* x_in, const float* ybuf_prev, float* x_out, int Tn,
+int run_block(moe_verify_ctx* c, int l, const float* x_in, const void* ybuf_prev, float* x_out, int Tn,
               hipStream_t st) {
   const moe_verify_config& g = c->cfg;
   const int E = g.n_routed, S = g.n_shared, k = g.top_k, KS = k + S, H = g.hidden, I = g.inter;
@@ -355,7 +355,7 @@ MV_API int moe_verify_init(const moe_verify_config* cfg, const moe_verify_weight
   A(&c->chunk_cnt, (size_t)mv::plan_chunks(g.max_positions, k) * 64 * sizeof(int32_t));
   // h and ybuf rows: every slot's row plus one sink row for the tiled GEMM's padding stores
   A(&c->h, (P * KS + 1) * I * es);
-  A(&c->ybuf, (P * KS + 1) * H * sizeof(float));
+  A(&c->ybuf, (P * KS + 1) * H * es);
   if (g.vocab > 0) A(&c->part, P * c->n_pg_lm * sizeof(mv::Top2));
   A(&c->counts, (size_t)L * E * sizeof(int32_t));
   if (ae != hipSuccess) {
@@ -468,7 +468,7 @@ MV_API int moe_verify_debug_layer(moe_verify_ctx* c, int32_t layer, const float*
   if (rc) return rc;
   const int KS = g.top_k + g.n_shared;
   if (moe_out)
-    MV_CHECK(mv::launch_combine(c->ybuf, c->slot_row, c->topk_w, T, g.hidden, g.top_k, g.n_shared, !use_tiled(g, T),
+    MV_CHECK(mv::launch_combine(g.wdtype, c->ybuf, c->slot_row, c->topk_w, T, g.hidden, g.top_k, g.n_shared, !use_tiled(g, T),
                                 moe_out, st));
   const size_t kb = (size_t)T * g.top_k * 4;
   if (topk_id) MV_CHECK(hipMemcpyAsync(topk_id, c->topk_id, kb, hipMemcpyDeviceToDevice, st));

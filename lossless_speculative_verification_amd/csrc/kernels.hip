@@ -81,6 +81,14 @@ __global__ void k_repack_router(const uint8_t* __restrict__ src, uint4* __restri
 
 // ============================================================================ norm + router + top-k
 
+// Four consecutive elements of the element type (float4 index i4) widened to float32.
+__device__ __forceinline__ float4 load4(const float* p, size_t i4) { return reinterpret_cast<const float4*>(p)[i4]; }
+__device__ __forceinline__ float4 load4(const uint16_t* p, size_t i4) {
+  const uint2 w = reinterpret_cast<const uint2*>(p)[i4];
+  return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u), __uint_as_float(w.y << 16),
+                     __uint_as_float(w.y & 0xFFFF0000u));
+}
+
 // Four consecutive elements (one float4 of the residual row) stored as the element type.
 __device__ __forceinline__ void store4(float* p, size_t i4, float4 u) { reinterpret_cast<float4*>(p)[i4] = u; }
 __device__ __forceinline__ void store4(uint16_t* p, size_t i4, float4 u) {
@@ -118,7 +126,7 @@ __device__ __forceinline__ void store4_perm(uint16_t* p, size_t i4, float4 u) {
 // Loads never sit behind a branch (the compiler would then wait for every load in
 // flight at the join): indices past the end are clamped and their values masked.
 template <typename T, bool ROUTE, int NP, int VM>
-__global__ __launch_bounds__(256) void k_norm_route(const float* x_in, const float* __restrict__ ybuf,
+__global__ __launch_bounds__(256) void k_norm_route(const float* x_in, const T* __restrict__ ybuf,
                                                     const int32_t* __restrict__ slot_row,
                                                     float* x_out, float* __restrict__ x_copy,
                                                     T* __restrict__ a_out, const uint4* __restrict__ wr,
@@ -156,7 +164,6 @@ __global__ __launch_bounds__(256) void k_norm_route(const float* x_in, const flo
     const float4* xi = reinterpret_cast<const float4*>(x_in) + (size_t)t * H4;
     float4 v[VM];
     if (ybuf) {
-      const float4* yb = reinterpret_cast<const float4*>(ybuf);
       const int KS = k + S;
       float4 m[VM];
 #pragma unroll
@@ -174,7 +181,7 @@ __global__ __launch_bounds__(256) void k_norm_route(const float* x_in, const flo
                                        : (sl < k ? (size_t)rr : (size_t)Tn * k + (size_t)(sl - k) * Tn + t);
           gt[s] = sl < k ? gr : 1.0f;
 #pragma unroll
-          for (int j = 0; j < VM; ++j) y[s][j] = yb[row * H4 + min(lane + kWave * j, H4 - 1)];
+          for (int j = 0; j < VM; ++j) y[s][j] = load4(ybuf, row * H4 + min(lane + kWave * j, H4 - 1));
         }
 #pragma unroll
         for (int s = 0; s < SB; ++s)
@@ -311,7 +318,7 @@ __global__ __launch_bounds__(256) void k_norm_route(const float* x_in, const flo
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 template <typename T, bool ROUTE, int NP, int VQ, int NC>
-__global__ __launch_bounds__(ROUTE ? 512 : 256) void k_norm_route_split(const float* x_in, const float* __restrict__ ybuf,
+__global__ __launch_bounds__(ROUTE ? 512 : 256) void k_norm_route_split(const float* x_in, const T* __restrict__ ybuf,
                                                           const int32_t* __restrict__ slot_row,
                                                           float* x_out, float* __restrict__ x_copy,
                                                           T* __restrict__ a_out, const uint4* __restrict__ wr,
@@ -407,8 +414,7 @@ __global__ __launch_bounds__(ROUTE ? 512 : 256) void k_norm_route_split(const fl
 #pragma unroll
         for (int j = 0; j < VQ; ++j) x[j] = xi[col[j]];
         if (ybuf) {
-          const float4* yb = reinterpret_cast<const float4*>(ybuf);
-          const int KS = k + S;
+              const int KS = k + S;
           float4 m[VQ];
 #pragma unroll
           for (int j = 0; j < VQ; ++j) m[j] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -425,7 +431,7 @@ __global__ __launch_bounds__(ROUTE ? 512 : 256) void k_norm_route_split(const fl
                                            : (sl < k ? (size_t)rr : (size_t)Tn * k + (size_t)(sl - k) * Tn + t);
               gt[s] = sl < k ? gr : 1.0f;
 #pragma unroll
-              for (int j = 0; j < VQ; ++j) y[s][j] = yb[row * H4 + col[j]];
+              for (int j = 0; j < VQ; ++j) y[s][j] = load4(ybuf, row * H4 + col[j]);
             }
 #pragma unroll
             for (int s = 0; s < SB; ++s)
@@ -847,9 +853,9 @@ __device__ __forceinline__ void moe_stream(const GemmArgs& g, int e, int row0, i
           const int r = mt * 16 + rg + i;
           const int dr = __shfl(dst_row, r, kWave);
           if (r < M) {
-            float* yrow = g.ybuf + (size_t)dr * g.H + (2 * q) * 16 + col;
-            yrow[0] = acc[p][mt][0][i];
-            yrow[16] = acc[p][mt][1][i];
+            T* yrow = reinterpret_cast<T*>(g.ybuf) + (size_t)dr * g.H + (2 * q) * 16 + col;
+            store_elem(yrow, 0, acc[p][mt][0][i]);
+            store_elem(yrow, 16, acc[p][mt][1][i]);
           }
         }
     }
@@ -1212,20 +1218,20 @@ __global__ void k_accept(const int32_t* __restrict__ drafts, const int32_t* __re
 }
 
 // m[t] = sum_j gate_j * y(t, j) in slot order (the block output before the residual add).
-__global__ void k_combine(const float* __restrict__ ybuf, const int32_t* __restrict__ slot_row,
+template <typename T>
+__global__ void k_combine(const T* __restrict__ ybuf, const int32_t* __restrict__ slot_row,
                           const float* __restrict__ gate, int Tn, int H, int k, int S, int pos_major,
                           float* __restrict__ m) {
   const int H4 = H >> 2;
   const size_t total = (size_t)Tn * H4;
   for (size_t u = (size_t)blockIdx.x * blockDim.x + threadIdx.x; u < total; u += (size_t)gridDim.x * blockDim.x) {
     const size_t t = u / H4, i = u % H4;
-    const float4* yb = reinterpret_cast<const float4*>(ybuf);
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int j = 0; j < k + S; ++j) {
       const size_t row = pos_major ? t * (size_t)(k + S) + j
                                    : (j < k ? (size_t)slot_row[t * k + j] : (size_t)Tn * k + (size_t)(j - k) * Tn + t);
       const float gt = j < k ? gate[t * k + j] : 1.0f;
-      const float4 y = yb[row * H4 + i];
+      const float4 y = load4(ybuf, row * H4 + i);
       s.x = fmaf(gt, y.x, s.x);
       s.y = fmaf(gt, y.y, s.y);
       s.z = fmaf(gt, y.z, s.z);
@@ -1269,7 +1275,7 @@ size_t norm_lds_bytes(int wdtype, int H, int np) {
 }
 
 template <typename T, int NP, int VM>
-static void norm_route_t(bool route, const float* x_in, const float* ybuf, const int32_t* slot_row, float* x_out,
+static void norm_route_t(bool route, const float* x_in, const T* ybuf, const int32_t* slot_row, float* x_out,
                          float* x_copy, void* a_out, const uint4* w, const float* bias, int32_t* topk_id,
                          float* topk_w, int Tn, int H, int S, int E, int k, float eps, int perm_a, int pos_major,
                          hipStream_t stream) {
@@ -1286,7 +1292,7 @@ static void norm_route_t(bool route, const float* x_in, const float* ybuf, const
 }
 
 template <typename T, int NP, int VQ>
-static void norm_split_t(bool route, const float* x_in, const float* ybuf, const int32_t* slot_row, float* x_out,
+static void norm_split_t(bool route, const float* x_in, const T* ybuf, const int32_t* slot_row, float* x_out,
                          float* x_copy, void* a_out, const uint4* w, const float* bias, int32_t* topk_id,
                          float* topk_w, int Tn, int H, int S, int E, int k, float eps, int perm_a, int pos_major,
                          hipStream_t stream) {
@@ -1305,7 +1311,7 @@ static void norm_split_t(bool route, const float* x_in, const float* ybuf, const
 }
 
 template <typename T, int NP>
-static void norm_split_np(bool route, const float* x_in, const float* ybuf, const int32_t* slot_row, float* x_out,
+static void norm_split_np(bool route, const float* x_in, const T* ybuf, const int32_t* slot_row, float* x_out,
                           float* x_copy, void* a_out, const uint4* w, const float* bias, int32_t* topk_id,
                           float* topk_w, int Tn, int H, int S, int E, int k, float eps, int perm_a, int pos_major,
                           hipStream_t stream) {
@@ -1317,7 +1323,7 @@ static void norm_split_np(bool route, const float* x_in, const float* ybuf, cons
 }
 
 template <typename T>
-static void norm_split(bool route, const float* x_in, const float* ybuf, const int32_t* slot_row, float* x_out,
+static void norm_split(bool route, const float* x_in, const T* ybuf, const int32_t* slot_row, float* x_out,
                        float* x_copy, void* a_out, const uint4* w, const float* bias, int32_t* topk_id,
                        float* topk_w, int Tn, int H, int S, int E, int k, float eps, int perm_a, int pos_major,
                        hipStream_t stream) {
@@ -1328,7 +1334,7 @@ static void norm_split(bool route, const float* x_in, const float* ybuf, const i
 }
 
 template <typename T, int NP>
-static void norm_route_np(bool route, const float* x_in, const float* ybuf, const int32_t* slot_row, float* x_out,
+static void norm_route_np(bool route, const float* x_in, const T* ybuf, const int32_t* slot_row, float* x_out,
                           float* x_copy, void* a_out, const uint4* w, const float* bias, int32_t* topk_id,
                           float* topk_w, int Tn, int H, int S, int E, int k, float eps, int perm_a, int pos_major,
                           hipStream_t stream) {
@@ -1339,7 +1345,7 @@ static void norm_route_np(bool route, const float* x_in, const float* ybuf, cons
   else norm_route_t<T, NP, 16>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, pos_major, stream);
 }
 
-hipError_t launch_norm_route(int wdtype, bool route, const float* x_in, const float* ybuf,
+hipError_t launch_norm_route(int wdtype, bool route, const float* x_in, const void* ybuf,
                              const int32_t* slot_row, float* x_out, float* x_copy, void* a_out, const void* wr,
                              const float* bias, int32_t* topk_id, float* topk_w, int Tn, int H, int S, int E,
                              int k, float eps, bool perm_a, bool pos_major, hipStream_t stream) {
@@ -1347,11 +1353,11 @@ hipError_t launch_norm_route(int wdtype, bool route, const float* x_in, const fl
   // the no-router combine (the final norm) runs split at every size
   const bool big = route && Tn >= kNormSplitMaxPositions;
   if (wdtype == 1) {
-    if (big) norm_route_np<uint16_t, 16>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, pos_major, stream);
-    else norm_split<uint16_t>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, pos_major, stream);
+    if (big) norm_route_np<uint16_t, 16>(route, x_in, static_cast<const uint16_t*>(ybuf), slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, pos_major, stream);
+    else norm_split<uint16_t>(route, x_in, static_cast<const uint16_t*>(ybuf), slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, pos_major, stream);
   } else {
-    if (big) norm_route_np<float, 16>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, pos_major, stream);
-    else norm_split<float>(route, x_in, ybuf, slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, pos_major, stream);
+    if (big) norm_route_np<float, 16>(route, x_in, static_cast<const float*>(ybuf), slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, pos_major, stream);
+    else norm_split<float>(route, x_in, static_cast<const float*>(ybuf), slot_row, x_out, x_copy, a_out, w, bias, topk_id, topk_w, Tn, H, S, E, k, eps, perm_a, pos_major, stream);
   }
   return hipGetLastError();
 }
@@ -1406,10 +1412,15 @@ hipError_t launch_accept(const int32_t* drafts, const int32_t* argmax, int B, in
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const float* ybuf, const int32_t* slot_row, const float* gate, int Tn, int H, int k,
-                          int S, bool pos_major, float* m, hipStream_t stream) {
-  k_combine<<<grid_for((size_t)Tn * (H / 4), 256), 256, 0, stream>>>(ybuf, slot_row, gate, Tn, H, k, S,
-                                                                      pos_major ? 1 : 0, m);
+hipError_t launch_combine(int wdtype, const void* ybuf, const int32_t* slot_row, const float* gate, int Tn, int H,
+                          int k, int S, bool pos_major, float* m, hipStream_t stream) {
+  const unsigned grid = grid_for((size_t)Tn * (H / 4), 256);
+  if (wdtype == 1)
+    k_combine<<<grid, 256, 0, stream>>>(static_cast<const uint16_t*>(ybuf), slot_row, gate, Tn, H, k, S,
+                                        pos_major ? 1 : 0, m);
+  else
+    k_combine<<<grid, 256, 0, stream>>>(static_cast<const float*>(ybuf), slot_row, gate, Tn, H, k, S,
+                                        pos_major ? 1 : 0, m);
   return hipGetLastError();
 }
 

@@ -39,7 +39,7 @@ struct GemmArgs {
   int Tn;                  // positions in this pass
   int k, E, KS, H, I;      // top-k, routed experts, k + shared, hidden, intermediate
   void* h;                 // UP out: h[rows][I]
-  float* ybuf;             // DOWN out: ybuf[rows][H], row r = the expert output of row r of h
+  void* ybuf;              // DOWN out: ybuf[rows][H] in the weight element type, one row per slot
   Top2* part;              // LM out: part[T][n_pg]
   int n_pg;                // LM: workgroups along the vocabulary (each 4 * lm_ppw pairs)
   int lm_ppw;              // LM: column pairs per wavefront
@@ -66,7 +66,7 @@ hipError_t launch_repack_router(const void* src, void* dst, int L, int E, int ro
 // when pos_major, else gathered through slot_row) + residual + RMSNorm (+ router and
 // top-k when route, overwriting topk_id/topk_w); a_out in the stage-ordered row layout
 // when perm_a (bf16 only).
-hipError_t launch_norm_route(int wdtype, bool route, const float* x_in, const float* ybuf,
+hipError_t launch_norm_route(int wdtype, bool route, const float* x_in, const void* ybuf,
                              const int32_t* slot_row, float* x_out, float* x_copy, void* a_out, const void* wr,
                              const float* bias, int32_t* topk_id, float* topk_w, int Tn, int H, int S, int E,
                              int k, float eps, bool perm_a, bool pos_major, hipStream_t stream);
@@ -94,8 +94,9 @@ hipError_t launch_argmax_reduce(const Top2* part, int n_pg, int Tn, int32_t* arg
 hipError_t launch_accept(const int32_t* drafts, const int32_t* argmax, int B, int K, int32_t* accepted,
                          int32_t* committed, hipStream_t stream);
 // m[t] = sum_j gate[t][j] * y(t, j) + sum_s y(t, k + s), with y(t, j) = ybuf[t*(k+S) + j]
-// when pos_major, else ybuf[slot_row[t*k + j]] (j < k) and ybuf[T*k + s*T + t] (shared).
-hipError_t launch_combine(const float* ybuf, const int32_t* slot_row, const float* gate, int Tn, int H, int k,
-                          int S, bool pos_major, float* m, hipStream_t stream);
+// when pos_major, else ybuf[slot_row[t*k + j]] (j < k) and ybuf[T*k + s*T + t] (shared);
+// ybuf holds the weight element type (bf16 when wdtype is 1).
+hipError_t launch_combine(int wdtype, const void* ybuf, const int32_t* slot_row, const float* gate, int Tn, int H,
+                          int k, int S, bool pos_major, float* m, hipStream_t stream);
 
 }  // namespace mv

@@ -4,7 +4,7 @@
 // The products are those of the verify step's MoE block (pages: "jina-ocr-v1" model page,
 // architecture paragraph: 64 routed + 2 shared SwiGLU experts, top-6 routing):
 //   UP:   h = bf16(silu(A W_gate^T) * (A W_up^T)) for the expert's rows of A
-//   DOWN: y = h W_down^T, written to the same row of ybuf as the row of h
+//   DOWN: y = bf16(h W_down^T), written to the same row of ybuf as the row of h
 // with the same row space, work list, outputs and float32 accumulation as the
 // streaming kernels (k_moe_gemm), so either path can run any block.
 #include "launch.h"
@@ -29,8 +29,8 @@ namespace mv {
 //
 // The MFMA takes the weights as its first operand and the activations as its second, so
 // lane l of a 16x16 result holds position 16*i + l % 16 and the four consecutive output
-// columns 4*(l/16)..+3: the epilogue stores 8 bytes (UP, bf16) or 16 bytes (DOWN, fp32)
-// per lane and row, no LDS round trip.
+// columns 4*(l/16)..+3: the epilogue stores 8 bytes (four bf16) per lane and row, no LDS
+// round trip.
 //
 // Pipeline: kTileStages = 4 LDS stages in a ring. Step st multiplies stage st from
 // registers while stage st + 1's operands are read from LDS and stages st + 2 .. st + 4
@@ -210,8 +210,9 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_moe_tiled(GemmArgs g) {
             const int col = (2 * q + tt) * 16 + c4;
             const size_t off = row_ok && q < g.NQ && col < g.H ? (size_t)(t.row0 + r) * g.H + col
                                                                : (size_t)g.sink_row * g.H;
-            *reinterpret_cast<float4*>(g.ybuf + off) =
-                make_float4(acc[i][pp][tt][0], acc[i][pp][tt][1], acc[i][pp][tt][2], acc[i][pp][tt][3]);
+            const uint32_t v0 = f32_to_bf16(acc[i][pp][tt][0]), v1 = f32_to_bf16(acc[i][pp][tt][1]);
+            const uint32_t v2 = f32_to_bf16(acc[i][pp][tt][2]), v3 = f32_to_bf16(acc[i][pp][tt][3]);
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(g.ybuf) + off) = make_uint2(v0 | (v1 << 16), v2 | (v3 << 16));
           }
         }
       }

@@ -33,8 +33,10 @@ the design notes):
 7. blocks are pre-norm: x <- x + MoE(RMSNorm(x)), RMSNorm with gamma 1 and eps
    inside the square root, and a final RMSNorm before the LM head;
 8. for bf16 weights, bf16 is materialised at the RMSNorm output (the input of the
-   router, the experts and the LM head) and at the SwiGLU output; the residual
-   stream is float32; everything else is exact (float64 here);
+   router, the experts and the LM head), at the SwiGLU output and at each expert's
+   output (the down projection's result, before its gate), as a BF16 checkpoint run
+   under Transformers or vLLM produces them; the residual stream is float32;
+   everything else is exact (float64 here);
 9. acceptance: the longest prefix of drafts equal to the verifier's argmax at the
    matching positions is accepted, and the verifier's token after it is added.
 """
@@ -124,15 +126,17 @@ def silu(z) -> np.ndarray:
     return z / (1.0 + np.exp(-z))
 
 
-def expert_ffn(a_rows, w_gate, w_up, w_down, round_h: bool) -> np.ndarray:
+def expert_ffn(a_rows, w_gate, w_up, w_down, round_bf16_io: bool) -> np.ndarray:
     """One SwiGLU expert on a set of positions (reading 6): (silu(a Wg^T) * (a Wu^T)) Wd^T.
 
-    The SwiGLU product is rounded to bf16 when the weights are bf16 (reading 8).
+    With round_bf16_io (bf16 weights, reading 8) the SwiGLU product and the expert's
+    output are rounded to bf16.
     """
     h = silu(a_rows @ w_gate.T) * (a_rows @ w_up.T)
-    if round_h:
+    if round_bf16_io:
         h = round_bf16(h)
-    return h @ w_down.T
+    y = h @ w_down.T
+    return round_bf16(y) if round_bf16_io else y
 
 
 def moe_layer(cfg, weights, layer: int, x) -> dict:

@@ -188,6 +188,8 @@ def _dense_reference_layer(cfg, wts, x):
         if cfg.wdtype == "bf16":
             h = h.float().to(torch.bfloat16).double()
         y = h @ f64(wts.w_down[0, e]).T
+        if cfg.wdtype == "bf16":
+            y = y.float().to(torch.bfloat16).double()
         m += (G[:, e:e + 1] if e < E else 1.0) * y
     return m.numpy()
 
