@@ -245,6 +245,19 @@ def test_skewed_step_sampled():
     log(f"  hot-expert slot fraction (sample) {hot:.3f}")
 
 
+def test_skewed_streaming_step():
+    """Hot experts on a decode-sized pass (128 positions, the streaming path, whose gate/up
+    GEMM builds the routing plan itself): experts with more than one 32-row work item."""
+    wl = WL["skewed_b128_k3"].with_(name="skewed_b32_k3", batch=32)
+    x = W.make_hidden(wl)
+    ref = oracle_step(wl)
+    most = max(int(np.bincount(l["ids"].ravel(), minlength=wl.n_routed).max()) for l in ref["layers"])
+    log(f"  largest per-expert slot count {most}")
+    assert most > 32, "the case must give some expert more than one work item"
+    ids, margin, hout = run_step(wl)
+    _check_step(wl, ref, ids, margin, hout, x, min_decisive=5)
+
+
 # ----------------------------------------------------------------------------- prefill shape
 
 
