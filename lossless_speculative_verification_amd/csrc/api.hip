@@ -327,7 +327,7 @@ MV_API int moe_verify_init(const moe_verify_config* cfg, const moe_verify_weight
   c->NQ_up = I / 16;
   c->NQ_dn = (H + 31) / 32;
   c->NQ_lm = (g.vocab + 31) / 32;
-  c->n_pg_lm = (c->NQ_lm + mv::kGemmWaves - 1) / mv::kGemmWaves;
+  c->n_pg_lm = (c->NQ_lm + mv::kLmWaves - 1) / mv::kLmWaves;
   c->router_units_per_layer = (size_t)(H * es / 16) * 64;
   c->up_units_per_layer = (size_t)(E + S) * c->NQ_up * c->NKB_H * mv::kPairUnits;
   c->down_units_per_layer = (size_t)(E + S) * c->NQ_dn * c->NKB_I * mv::kPairUnits;
@@ -417,13 +417,13 @@ MV_API int moe_verify_step(moe_verify_ctx* c, const float* hidden_in, int32_t B,
                                  g.n_shared, g.n_routed, g.top_k, g.rms_eps, false, !use_tiled(g, Tn), st));
   c->prof_end(st);
   if (g.vocab > 0) {
-    // Workgroups (4 wavefronts, two per CU) cover one row block of up to kLmRows
+    // Workgroups (kLmWaves wavefronts, one per CU) cover one row block of up to kLmRows
     // positions; pairs per wavefront so that the workgroups of one row block make about
     // one round on the device (further row blocks share the weight stream through L2).
     const int n_items = (Tn + mv::kLmRows - 1) / mv::kLmRows;
-    const int target = c->n_cu * mv::kGemmWaves * 2;  // pair streams per round
+    const int target = c->n_cu * mv::kLmWaves;  // pair streams per round
     const int ppw = std::max(1, (c->NQ_lm + target - 1) / target);
-    const int n_pg = (c->NQ_lm + mv::kGemmWaves * ppw - 1) / (mv::kGemmWaves * ppw);
+    const int n_pg = (c->NQ_lm + mv::kLmWaves * ppw - 1) / (mv::kLmWaves * ppw);
     mv::GemmArgs a{};
     a.A = c->a;
     a.B = c->lm_p;

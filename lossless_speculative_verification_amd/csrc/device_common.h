@@ -33,6 +33,7 @@ constexpr int kStreamWavesUp = 4;
 constexpr int kStreamWavesDown = 1;
 constexpr int kGemmMB = 16 * MV_GEMM_NMT;           // rows per expert GEMM work item
 constexpr int kLmRows = 128;                        // positions per LM-head row block
+constexpr int kLmWaves = 8;                          // wavefronts per LM-head workgroup (one workgroup per CU)
 constexpr int kSelfPlanMaxSlots = 4096;      // routed slots up to which the streaming gate/up plans itself
 constexpr int kNormSplitMaxPositions = 4096;  // passes below this use the split norm/router kernel
 constexpr int kTileM = 256;                         // rows per work item of the LDS-tiled expert GEMM

@@ -999,9 +999,12 @@ __global__ __launch_bounds__(kWave * WPG, MV_GEMM_WAVES_PER_SIMD) void k_moe_gem
   }
 }
 
-// LM head. A workgroup of 4 wavefronts covers 4*ppw consecutive column pairs (wavefront
-// w: pairs w*ppw ..) for one row block of up to 16*NMT <= kLmRows positions, so every
-// weight byte is read once per row block (at most 128 positions need one row block).
+// LM head. A workgroup of kLmWaves wavefronts (one workgroup per compute unit) covers
+// kLmWaves*ppw consecutive column pairs (wavefront w: pairs w*ppw ..) for one row block of
+// up to 16*NMT <= kLmRows positions, so every weight byte is read once per row block (at
+// most 128 positions need one row block). The block's rows are staged once per K block for
+// all the workgroup's wavefronts: eight wavefronts per compute unit in one workgroup read
+// half the activation bytes that two workgroups of four would.
 // The block's normalised rows are staged in LDS one 256-byte K block at a time (double
 // buffered, read one K block ahead in registers) and shared by the 4 wavefronts.
 // Weights stream as in moe_stream, two K blocks in flight; no load in the main loop
@@ -1018,22 +1021,24 @@ __device__ __forceinline__ void lm_stream(const GemmArgs& g, int row0, int M, in
                                           uint4 (*As)[kLmRows][kChunksPerRow + 1],
                                           Top2 (*red)[kLmRows]) {
   constexpr int MB = NMT * 16;
-  constexpr int AL = MB * kChunksPerRow / 256;  // 16-byte A chunks per thread per K block
-  static_assert(AL >= 1, "row blocks have at least 16 rows");
+  constexpr int NTH = kLmWaves * kWave;
+  constexpr int RPS = NTH / kChunksPerRow;           // rows one staging pass covers
+  constexpr int AL = (MB + RPS - 1) / RPS;            // 16-byte A chunks per thread per K block
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int row_units = g.K * (int)sizeof(T) / 16;
   const int NKB = row_units / kChunksPerRow;
-  const int q0 = (pg * kGemmWaves + wave) * ppw;
+  const int q0 = (pg * kLmWaves + wave) * ppw;
   const float NEG = -__builtin_huge_valf();
   const int F = ppw * NKB;
 
-  // A staging: thread -> (row srow + 16*j, chunk schunk) of the K block; AL chunks.
+  // A staging: thread -> (row srow + RPS*j, chunk schunk) of the K block; AL chunks (the
+  // threads past a small block's last row stage nothing).
   const int srow = threadIdx.x >> 4, schunk = threadIdx.x & 15;
   const u32x4_t* abase = reinterpret_cast<const u32x4_t*>(g.A) + schunk;
   int aoff[AL];  // 16-byte offset of each staged row (a block's rows past M repeat its first)
 #pragma unroll
   for (int j = 0; j < AL; ++j) {
-    const int r = srow + 16 * j;
+    const int r = srow + RPS * j;
     aoff[j] = (row0 + (r < M ? r : 0)) * row_units;
   }
   // A block f+1 waits in ra while block f is in LDS.
@@ -1048,7 +1053,8 @@ __device__ __forceinline__ void lm_stream(const GemmArgs& g, int row0, int M, in
   };
   auto write_a = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < AL; ++j) *reinterpret_cast<u32x4_t*>(&As[buf][srow + 16 * j][schunk]) = ra[j];
+    for (int j = 0; j < AL; ++j)
+      if (srow + RPS * j < MB) *reinterpret_cast<u32x4_t*>(&As[buf][srow + RPS * j][schunk]) = ra[j];
   };
 
   // Pairs past the vocabulary's last pair stream a copy of it; their columns are masked.
@@ -1151,15 +1157,15 @@ __device__ __forceinline__ void lm_stream(const GemmArgs& g, int row0, int M, in
     const int r = threadIdx.x;
     Top2 rec = red[0][r];
 #pragma unroll
-    for (int w = 1; w < kGemmWaves; ++w) rec = top2_merge(rec, red[w][r]);
+    for (int w = 1; w < kLmWaves; ++w) rec = top2_merge(rec, red[w][r]);
     g.part[(size_t)(row0 + r) * g.n_pg + pg] = rec;
   }
 }
 
 template <typename T>
-__global__ __launch_bounds__(256, 2) void k_lm_head(GemmArgs g) {
+__global__ __launch_bounds__(kLmWaves * kWave, 1) void k_lm_head(GemmArgs g) {
   __shared__ uint4 As[2][kLmRows][kChunksPerRow + 1];
-  __shared__ Top2 red[kGemmWaves][kLmRows];
+  __shared__ Top2 red[kLmWaves][kLmRows];
   const int n_items = (g.Tn + kLmRows - 1) / kLmRows;
   const int n = n_items * g.n_pg;
   if ((int)blockIdx.x >= n) return;  // workgroup-uniform
@@ -1382,7 +1388,7 @@ static void gemm_t(int epi, const GemmArgs& args, unsigned n_wg, hipStream_t str
     k_moe_gemm<T, EPI_UP, MV_GEMM_NMT, MV_GEMM_D, kStreamWavesUp><<<grid, dim3(kWave * kStreamWavesUp), 0, stream>>>(args);
   else if (epi == EPI_DOWN)
     k_moe_gemm<T, EPI_DOWN, MV_GEMM_NMT, MV_GEMM_D, kStreamWavesDown><<<grid, dim3(kWave * kStreamWavesDown), 0, stream>>>(args);
-  else k_lm_head<T><<<grid, dim3(256), 0, stream>>>(args);
+  else k_lm_head<T><<<grid, dim3(kLmWaves * kWave), 0, stream>>>(args);
 }
 
 hipError_t launch_gemm_planned(int wdtype, const GemmArgs& args, unsigned n_wg, hipStream_t stream) {
