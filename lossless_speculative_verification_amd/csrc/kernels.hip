@@ -8,12 +8,16 @@
 // choices plus the verifier's next token.
 //
 // Kernel sequence per pass (one HIP stream, no host round trip):
-//   per block l: k_norm_route  (combine of block l-1 + residual + RMSNorm + router + top-k)
-//                k_plan        (expert-major stable ordering of the T*k routed slots + work list)
-//                k_gemm<UP>    (gate/up projections + SwiGLU, MFMA, weights streamed once)
-//                k_gemm<DOWN>  (down projection, gate scaling, one ybuf row per slot)
-//   then         k_norm_route  (final combine + residual + RMSNorm, no router)
-//                k_gemm<LM>    (LM-head logits tile by tile, top-1/top-2 per tile, never stored)
+//   per block l: k_norm_route_split / k_norm_route
+//                               (combine of block l-1 + residual + RMSNorm + router + top-k)
+//                k_plan        (expert-major stable ordering of the T*k routed slots + work
+//                               list; built inside k_moe_gemm_planned on small streaming passes)
+//                k_moe_gemm_planned / k_moe_gemm<UP> / k_moe_tiled<UP>
+//                              (gate/up projections + SwiGLU, MFMA; tiled.hip for large passes)
+//                k_moe_gemm<DOWN> / k_moe_tiled<DOWN>
+//                              (down projection, one bf16 (or fp32) ybuf row per slot)
+//   then         k_norm_route_split (final combine + residual + RMSNorm, no router)
+//                k_lm_head     (LM-head logits tile by tile, top-1/top-2 per tile, never stored)
 //                k_argmax_reduce
 //   and          k_accept
 #include <climits>
@@ -1270,8 +1274,6 @@ hipError_t launch_repack_router(const void* src, void* dst, int L, int E, int ro
                                                              static_cast<uint4*>(dst), L, E, row_bytes);
   return hipGetLastError();
 }
-
-int norm_positions_per_wg(int Tn) { return Tn >= kNormSplitMaxPositions ? 16 : norm_split_positions(Tn); }
 
 int norm_split_positions(int Tn) { return Tn <= 512 ? 1 : (Tn <= 1024 ? 2 : 4); }
 

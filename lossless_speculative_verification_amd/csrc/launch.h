@@ -75,7 +75,7 @@ hipError_t launch_norm_route(int wdtype, bool route, const float* x_in, const vo
 // per chunk.
 hipError_t launch_plan(const PlanArgs& pa, hipStream_t stream);
 int plan_chunks(int Tn, int k);
-// One-dimensional grid of n_wg workgroups (item x column-pair group, see k_gemm).
+// One-dimensional grid of n_wg workgroups (item x column-pair group, see k_moe_gemm; LM head: k_lm_head).
 hipError_t launch_gemm(int wdtype, int epi, const GemmArgs& args, unsigned n_wg, hipStream_t stream);
 // Gate/up of the streaming path with the plan built in its prologue (no launch_plan), for
 // passes of at most kSelfPlanMaxSlots routed slots; same grid as launch_gemm(EPI_UP).
@@ -85,8 +85,8 @@ hipError_t launch_gemm_planned(int wdtype, const GemmArgs& args, unsigned n_wg, 
 // unit) share the tiles. Needs K >= 256 elements.
 hipError_t launch_gemm_tiled(int epi, const GemmArgs& args, unsigned n_wg, hipStream_t stream);
 int tiled_tiles_per_item(int NQ);
-// Positions per workgroup of the norm/router kernel and its dynamic LDS bytes.
-int norm_positions_per_wg(int Tn);
+// Positions per workgroup of the split norm/router kernel (passes below
+// kNormSplitMaxPositions) and the norm kernels' dynamic LDS bytes.
 int norm_split_positions(int Tn);
 size_t norm_lds_bytes(int wdtype, int H, int np);
 hipError_t launch_argmax_reduce(const Top2* part, int n_pg, int Tn, int32_t* argmax, float* margin,
