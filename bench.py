@@ -75,6 +75,92 @@ def cpu_baseline(wl, weights, x, drafts_fn):
                       f"head) and its acceptance, float64 numpy, {dt:.1f} s"}
 
 
+def _time(fn, steps, warmup):
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def sweep(args):
+    """Draft length K x batch B on the 12-block decode model (one weight set, one context).
+
+    The pages find that the best draft length depends on launch overhead (eager K=3 vs
+    graphs K=1 on an L4 at batch 1, "L4 speculative" paragraph of the model page). Here
+    every point is timed both as eager launches and as one replayed HIP graph; the
+    number of routed experts a block touches grows with the positions of a pass, which
+    sets the weight bytes per pass at small batch.
+    """
+    import torch
+
+    from lossless_speculative_verification_amd import binding as bnd
+    from lossless_speculative_verification_amd import workload as W
+
+    base = W.WORKLOADS["decode_b32_k3"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("[sweep] generating weights")
+    dw = bnd.upload_weights(W.make_weights(base), dev)
+    ctx = bnd.MoeVerify(base, dw, 32 * 4)
+    del dw
+    torch.cuda.empty_cache()
+    for B in (1, 4, 32):
+        for K in (0, 1, 3):
+            wl = base.with_(batch=B, drafts=K)
+            T = wl.positions
+            x = torch.from_numpy(W.make_hidden(wl)).to(dev)
+            ids = torch.empty(T, dtype=torch.int32, device=dev)
+            n_acc = torch.zeros(B, dtype=torch.int32, device=dev)
+            committed = torch.empty(B, K + 1, dtype=torch.int32, device=dev)
+            ctx.step(x, B, K, ids)
+            torch.cuda.synchronize()
+            counts = ctx.expert_counts()
+            drafts = torch.from_numpy(W.make_drafts(wl, ids.cpu().numpy())).to(dev)
+
+            def step():
+                ctx.step(x, B, K, ids)
+                bnd.accept_greedy(drafts, ids, B, K, n_acc, committed)
+
+            step()
+            torch.cuda.synchronize()
+            ref = (ids.clone(), n_acc.clone())
+            g = torch.cuda.CUDAGraph()
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                step()
+            torch.cuda.current_stream().wait_stream(s)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g):
+                step()
+            ids.fill_(-1)
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(ids, ref[0]) and torch.equal(n_acc, ref[1]), "graph replay differs from eager"
+            ms_graph = _time(g.replay, args.steps, args.warmup)
+            ms_eager = _time(step, args.steps, args.warmup)
+            com = int(n_acc.sum().item()) + B
+            acc = algorithmic(wl, counts)
+            line = {"sweep": "decode_kxb", "B": B, "K": K, "positions": T, "committed_per_step": com,
+                    "ms_graph": round(ms_graph, 4), "ms_eager": round(ms_eager, 4),
+                    "tokens_per_s_graph": round(com / (ms_graph * 1e-3), 1),
+                    "tokens_per_s_eager": round(com / (ms_eager * 1e-3), 1),
+                    "tokens_per_s_per_seq_graph": round(com / B / (ms_graph * 1e-3), 1),
+                    "touched_experts_per_block": acc["touched_per_block"],
+                    "hbm_frac_graph": round(acc["step_bytes"] / (ms_graph * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            print(json.dumps(line), flush=True)
+            del g
+    ctx.close()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -83,6 +169,9 @@ def main():
     ap.add_argument("--workload", default="decode_b32_k3")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time the 12-block decode model over K in {0,1,3} x B in {1,4,32}, HIP graph and eager "
+                         "(one JSON line per point instead of the bench line)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 256 MiB device to device (scale reference for the HBM byte counters)")
     args = ap.parse_args()
@@ -101,6 +190,10 @@ def main():
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the verify step is "
               "data-parallel over sequences with no exchange, see the design notes.", file=sys.stderr)
         sys.exit(2)
+
+    if args.sweep:
+        sweep(args)
+        return
 
     import torch
 
