@@ -16,7 +16,9 @@ Random streams: ``numpy.random.default_rng([seed, layer, tid, index])`` with
 
     tid 0 router, 1 gate, 2 up, 3 down (index = expert, shared experts after
           the routed ones), 4 LM head (layer = L, index = 1024-row chunk),
-    5 hidden states, 6 draft coin flips, 7 random draft ids (layer 0, index 0).
+    5 hidden states, 6 draft coin flips, 7 random draft ids (layer 0, index 0),
+    8 draft-block projection, 9 draft-block gate, 10 up, 11 down (layer = L + 1,
+          index 0).
 
 Weights are standard normal float32 draws times the standard deviation
 (float32 multiply), then rounded to bfloat16 by torch's round-to-nearest-even
@@ -33,6 +35,8 @@ from typing import Optional
 import numpy as np
 
 TID_ROUTER, TID_GATE, TID_UP, TID_DOWN, TID_LM, TID_HIDDEN, TID_COIN, TID_DRAFT = range(8)
+TID_MTP_PROJ, TID_MTP_GATE, TID_MTP_UP, TID_MTP_DOWN = range(8, 12)
+DRAFT_INTER = 1792  # intermediate width of the draft block's dense SwiGLU (chosen: 2 x 896)
 LM_CHUNK_ROWS = 1024
 
 
@@ -182,3 +186,26 @@ def make_drafts(wl: Workload, verifier_ids: np.ndarray) -> np.ndarray:
     coins = np.random.default_rng([wl.seed, 0, TID_COIN, 0]).random((B, K))
     ids = np.random.default_rng([wl.seed, 0, TID_DRAFT, 0]).integers(0, V, (B, K))
     return np.where(coins < wl.p_match, y[:, :K], ids).astype(np.int32)
+
+
+@dataclass
+class DraftWeights:
+    """Weights of the draft block (multi-token-prediction head) in the layouts its init
+    call takes: proj [H][2H] (input = [normalised hidden, normalised token embedding]),
+    w_gate, w_up [I_d][H], w_down [H][I_d]; bf16 bit patterns or float32 as the
+    verifier's. The token embedding is the verifier's LM-head matrix (tied)."""
+
+    wdtype: str
+    inter: int
+    proj: np.ndarray
+    w_gate: np.ndarray
+    w_up: np.ndarray
+    w_down: np.ndarray
+
+
+def make_draft_weights(wl: Workload, inter: int = DRAFT_INTER) -> DraftWeights:
+    """Seeded N(0, weight_std) draft-block weights for ``wl`` (streams tid 8..11, layer L + 1)."""
+    H, L = wl.hidden, wl.n_layers
+    d = lambda tid, shape: _draw(wl.seed, L + 1, tid, 0, shape, wl.weight_std, wl.wdtype)
+    return DraftWeights(wl.wdtype, inter, d(TID_MTP_PROJ, (H, 2 * H)), d(TID_MTP_GATE, (inter, H)),
+                        d(TID_MTP_UP, (inter, H)), d(TID_MTP_DOWN, (H, inter)))

@@ -38,7 +38,17 @@ the design notes):
    under Transformers or vLLM produces them; the residual stream is float32;
    everything else is exact (float64 here);
 9. acceptance: the longest prefix of drafts equal to the verifier's argmax at the
-   matching positions is accepted, and the verifier's token after it is added.
+   matching positions is accepted, and the verifier's token after it is added;
+10. the draft block (the pages name FastMTP, a multi-token-prediction head that drafts
+   three tokens ahead, without fixing its shape): one block applied K times. Step i
+   takes a hidden state h and a token t (at step 1 the verifier's residual stream,
+   before its final norm, at the last accepted position, and the last committed
+   token), forms [RMSNorm(h), RMSNorm(E[t])] with E the LM-head matrix (tied token
+   embedding), projects 2H -> H (bias-free), adds a pre-norm dense SwiGLU block with
+   a residual, applies the final RMSNorm and the shared LM head, and drafts the
+   greedy token; its hidden state and token feed step i + 1. bf16 is materialised
+   as in reading 8: the two normalised halves, the projection output, the block's
+   normalised input, its SwiGLU product and its output, and the LM-head input.
 """
 from __future__ import annotations
 
@@ -289,3 +299,48 @@ def speculative_decode(next_token: NextToken, draft: Callable[[List[int], int], 
         out += [int(v) for v in committed[0, : n[0] + 1]]
         passes += 1
     return out[: len(prompt) + n_new], passes
+
+
+# --------------------------------------------------------------------------- draft block
+
+
+def draft_inputs(hidden, accepted_len, committed, K: int):
+    """Inputs of the first draft step after a verifier pass (reading 10): per sequence b,
+    the verifier's hidden row b*(K+1) + n_b (n_b accepted drafts) and the last committed
+    token committed[b][n_b] (the verifier's own token after the accepted drafts)."""
+    n = np.asarray(accepted_len, np.int64)
+    B = n.shape[0]
+    hidden = np.asarray(hidden, np.float32).reshape(B, K + 1, -1)
+    com = np.asarray(committed, np.int64).reshape(B, K + 1)
+    rows = np.arange(B)
+    return hidden[rows, n], com[rows, n]
+
+
+def draft_step(cfg, weights, dweights, h, tok, K: int) -> dict:
+    """K recursive steps of the draft block (reading 10) for B sequences.
+
+    h [B,H] float32 hidden states, tok [B] tokens. Returns drafts [B,K] (int64),
+    margin [B,K] (top-1 minus top-2 LM logit of each draft) and hidden [K,B,H] (the
+    block's float32 output after each step, the next step's h).
+    """
+    bf = cfg.wdtype == "bf16"
+    rnd = round_bf16 if bf else (lambda v: np.asarray(v, np.float64))
+    wp = as_f64(dweights.proj, cfg.wdtype)
+    wg, wu, wd = (as_f64(w, cfg.wdtype) for w in (dweights.w_gate, dweights.w_up, dweights.w_down))
+    h = np.asarray(h, np.float32)
+    tok = np.asarray(tok, np.int64)
+    B = h.shape[0]
+    drafts = np.zeros((B, K), np.int64)
+    margins = np.zeros((B, K))
+    hidden = np.zeros((K, B, h.shape[1]), np.float32)
+    for i in range(K):
+        emb = as_f64(weights.lm_head[tok], cfg.wdtype)
+        u = np.concatenate([rnd(rms_norm(h, cfg.rms_eps)), rnd(rms_norm(emb, cfg.rms_eps))], axis=1)
+        x = rnd(u @ wp.T).astype(np.float32)               # projection output, the block's residual
+        a = rnd(rms_norm(x, cfg.rms_eps))
+        y = expert_ffn(a, wg, wu, wd, bf)                   # the same SwiGLU form as an expert
+        x = (x.astype(np.float64) + y).astype(np.float32)
+        ids, margin, _ = lm_head_argmax(final_norm(cfg, x), weights.lm_head, cfg.wdtype)
+        drafts[:, i], margins[:, i], hidden[i] = ids, margin, x
+        h, tok = x, ids
+    return {"drafts": drafts, "margin": margins, "hidden": hidden}

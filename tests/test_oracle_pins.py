@@ -384,3 +384,112 @@ def test_verify_step_rows_are_independent():
     part = O.verify_step(wl, wts, x[2:3])
     assert part["ids"][0] == full["ids"][2]
     np.testing.assert_allclose(part["hidden_out"][0], full["hidden_out"][2], rtol=0, atol=0)
+
+
+# ----------------------------------------------------------------------------- draft block
+
+
+def _draft_setup(inter=64):
+    wl = W.WORKLOADS["tiny_fp32"]
+    wts = W.make_weights(wl)
+    dw = W.make_draft_weights(wl, inter)
+    rng = np.random.default_rng(5)
+    h = rng.standard_normal((3, wl.hidden)).astype(np.float32)
+    tok = np.array([3, 500, 999])
+    return wl, wts, dw, h, tok
+
+
+def _zero_block(dw, proj):
+    return W.DraftWeights(dw.wdtype, dw.inter, proj.astype(dw.proj.dtype), np.zeros_like(dw.w_gate),
+                          np.zeros_like(dw.w_up), np.zeros_like(dw.w_down))
+
+
+def test_draft_embedding_half_repeats_the_token():
+    """Projection [0 | I] and a zero SwiGLU block: the block's output is the token's own
+    normalised embedding (a row of the LM head), whose own logit sqrt(H)*|E_t| (about
+    2.6 here) dominates every other row's (about N(0, 0.23)); so every draft repeats it."""
+    wl, wts, dw, h, tok = _draft_setup()
+    H = wl.hidden
+    proj = np.concatenate([np.zeros((H, H)), np.eye(H)], axis=1)
+    out = O.draft_step(wl, wts, _zero_block(dw, proj), h, tok, 3)
+    assert (out["drafts"] == tok[:, None]).all()
+    # and the hidden state after each step is the normalised embedding itself
+    emb = wts.lm_head[tok].astype(np.float64)
+    ref = emb / np.sqrt((emb ** 2).mean(axis=1, keepdims=True) + wl.rms_eps)
+    np.testing.assert_allclose(out["hidden"][0], ref, rtol=1e-6)
+
+
+def test_draft_hidden_half_is_the_verifier_head():
+    """Projection [I | 0] and a zero SwiGLU block: draft 1 is the LM head's greedy token
+    on the normalised hidden state (normalising twice changes it by at most eps)."""
+    wl, wts, dw, h, tok = _draft_setup()
+    H = wl.hidden
+    proj = np.concatenate([np.eye(H), np.zeros((H, H))], axis=1)
+    out = O.draft_step(wl, wts, _zero_block(dw, proj), h, tok, 1)
+    u = h.astype(np.float64) / np.sqrt((h.astype(np.float64) ** 2).mean(axis=1, keepdims=True))
+    logits = u @ wts.lm_head.astype(np.float64).T
+    assert (out["drafts"][:, 0] == np.argmax(logits, axis=1)).all()
+
+
+def test_draft_block_matches_torch_swiglu():
+    """One step against torch's rms_norm / silu in float64: x1 = z + SwiGLU(rms(z)) with
+    z = [rms(h), rms(E[t])] Wp^T, then the greedy token of rms(x1) W_lm^T."""
+    import torch
+    import torch.nn.functional as F
+
+    wl, wts, dw, h, tok = _draft_setup()
+    out = O.draft_step(wl, wts, dw, h, tok, 1)
+    t = lambda v: torch.from_numpy(np.asarray(v, np.float64))
+    H = wl.hidden
+    u = torch.cat([F.rms_norm(t(h), (H,), eps=wl.rms_eps), F.rms_norm(t(wts.lm_head[tok]), (H,), eps=wl.rms_eps)], 1)
+    z = (u @ t(dw.proj).T).float().double()
+    a = F.rms_norm(z, (H,), eps=wl.rms_eps)
+    x1 = z + (F.silu(a @ t(dw.w_gate).T) * (a @ t(dw.w_up).T)) @ t(dw.w_down).T
+    np.testing.assert_allclose(out["hidden"][0], x1.float().numpy(), rtol=1e-5, atol=1e-6)
+    ids = torch.argmax(F.rms_norm(x1.float().double(), (H,), eps=wl.rms_eps) @ t(wts.lm_head).T, dim=1)
+    assert (out["drafts"][:, 0] == ids.numpy()).all()
+
+
+def test_draft_steps_compose():
+    """K steps = K single steps, each fed the previous step's hidden state and draft."""
+    wl, wts, dw, h, tok = _draft_setup()
+    full = O.draft_step(wl, wts, dw, h, tok, 3)
+    hh, tt = h, tok
+    for i in range(3):
+        one = O.draft_step(wl, wts, dw, hh, tt, 1)
+        assert (one["drafts"][:, 0] == full["drafts"][:, i]).all()
+        np.testing.assert_array_equal(one["hidden"][0], full["hidden"][i])
+        hh, tt = one["hidden"][0], one["drafts"][:, 0]
+
+
+def test_draft_inputs_pick_the_last_accepted_row():
+    B, K, H = 4, 3, 5
+    hidden = np.arange(B * (K + 1) * H, dtype=np.float32).reshape(B * (K + 1), H)
+    n = np.array([0, 3, 1, 2])
+    com = np.array([[7, -1, -1, -1], [1, 2, 3, 4], [5, 6, -1, -1], [8, 9, 10, -1]])
+    hh, tt = O.draft_inputs(hidden, n, com, K)
+    for b in range(B):
+        np.testing.assert_array_equal(hh[b], hidden[b * (K + 1) + n[b]])
+        assert tt[b] == com[b, n[b]]
+    assert list(tt) == [7, 4, 6, 10]
+
+
+def test_speculative_with_the_draft_block_equals_greedy():
+    """The pages' invariant with the draft block as the drafter: it fixes the number of
+    passes, never the tokens."""
+    wl = W.WORKLOADS["tiny_fp32"]
+    wts = W.make_weights(wl)
+    dw = W.make_draft_weights(wl, 64)
+    nt = _toy_verifier(wl, wts, 31)
+
+    def hidden_of(prefix):  # the verifier's residual stream for the last position of prefix
+        x = np.random.default_rng([31, len(prefix)] + [int(t) for t in prefix]).standard_normal(
+            wl.hidden).astype(np.float32)
+        return O.verify_step(wl, wts, x[None])["hidden_out"]
+
+    def draft(prefix, k):
+        return O.draft_step(wl, wts, dw, hidden_of(prefix[:-1]), np.array([prefix[-1]]), k)["drafts"][0]
+
+    greedy = O.greedy_decode(nt, [2, 9], 24)
+    spec, passes = O.speculative_decode(nt, draft, [2, 9], 24, 3)
+    assert spec == greedy and passes <= 24
