@@ -145,6 +145,49 @@ const char *moe_verify_last_error(void);
 int moe_verify_debug_layer(moe_verify_ctx *ctx, int32_t layer, const float *x_in, int32_t T,
                            float *moe_out, int32_t *topk_id, float *topk_w, void *stream);
 
+/* ---- draft block: drafts the next pass's K tokens on the device ---------------------- */
+
+/* The draft block is a multi-token-prediction head ("jina-ocr-v1" model page, FastMTP
+ * paragraph: it drafts three tokens ahead for the verifier to check greedily). The pages
+ * do not give its shape; this library's reading: step i takes a hidden state h and a
+ * token t, forms [RMSNorm(h), RMSNorm(E[t])] with E the verifier's LM-head matrix (tied
+ * embedding), projects it 2H -> H (bias-free, output materialised in the weight type),
+ * adds a pre-norm dense SwiGLU block down(silu(gate a) * up a) with a residual, applies
+ * the final RMSNorm and the verifier's LM head, and drafts the greedy token (ties to the
+ * lower index); the block's output hidden state and the draft feed step i + 1. */
+
+/* Host struct of device pointers (element type = the context's wdtype), read only during
+ * moe_draft_init. inter: a multiple of 128 (bf16) or 64 (f32) in [16, 16384]. */
+typedef struct {
+  int32_t     inter;   /* I_d, SwiGLU intermediate width of the draft block          */
+  const void *proj;    /* [H][2H]: columns 0..H-1 act on RMSNorm(h), H..2H-1 on       */
+                       /*          RMSNorm(E[t])                                      */
+  const void *w_gate;  /* [I_d][H]                                                    */
+  const void *w_up;    /* [I_d][H]                                                    */
+  const void *w_down;  /* [H][I_d]                                                    */
+} moe_draft_weights;
+
+/* Attach draft-block weights to a context that has an LM head (vocab > 0): copy them
+ * into the library's layout on `stream`, allocate the block's workspace for
+ * max_positions sequences, and wait. Calling it again replaces the weights (buffers of
+ * earlier calls are freed by moe_verify_destroy). MOE_EINVAL for a context without an
+ * LM head or a NULL pointer, MOE_EUNSUPPORTED for an inter outside the limits. */
+int moe_draft_init(moe_verify_ctx *ctx, const moe_draft_weights *weights, void *stream);
+
+/* K draft steps for B sequences right after a verifier pass of Kv drafts:
+ *   hidden       [B*(Kv+1)][H] float32 device: that pass's hidden_out (required);
+ *   accepted_len [B] int32 device and committed [B][Kv+1] int32 device: accept_greedy's
+ *                outputs for that pass;
+ *   drafts       [B][K] int32 device out: the next pass's drafts.
+ * Step 1 of sequence b takes the hidden row b*(Kv+1) + n_b and the token
+ * committed[b][n_b] (n_b = accepted_len[b]); later steps take the previous step's output.
+ * B >= 1, Kv >= 0, K >= 1, B*(Kv+1) <= max_positions. Enqueues work on `stream` only (no
+ * synchronisation, allocation or host copy: graph-capturable). It uses the context's
+ * verify workspace, so it must not overlap a moe_verify_step on the same context. */
+int moe_draft_step(moe_verify_ctx *ctx, const float *hidden, const int32_t *accepted_len,
+                   const int32_t *committed, int32_t B, int32_t Kv, int32_t K, int32_t *drafts,
+                   void *stream);
+
 /* ---- measurement hooks (not on the verify path) ------------------------------------ */
 
 /* Kernel classes timed by the profiling hook, in this order. */

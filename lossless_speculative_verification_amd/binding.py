@@ -19,7 +19,8 @@ MOE_F32, MOE_BF16 = 0, 1
 
 EXPORTS = ("moe_verify_check_config", "moe_verify_check_step", "moe_verify_init", "moe_verify_step",
            "accept_greedy", "moe_verify_destroy", "moe_verify_last_error", "moe_verify_debug_layer",
-           "moe_verify_profile", "moe_verify_profile_read", "moe_verify_expert_counts")
+           "moe_verify_profile", "moe_verify_profile_read", "moe_verify_expert_counts", "moe_draft_init",
+           "moe_draft_step")
 PROF_KINDS = ("norm_route", "plan", "gemm_up", "gemm_down", "lm_head", "argmax")
 
 
@@ -33,6 +34,11 @@ class Config(ctypes.Structure):
 class WeightPtrs(ctypes.Structure):
     _fields_ = [("router_w", ctypes.c_void_p), ("router_bias", ctypes.c_void_p), ("w_gate", ctypes.c_void_p),
                 ("w_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p), ("lm_head", ctypes.c_void_p)]
+
+
+class DraftWeightPtrs(ctypes.Structure):
+    _fields_ = [("inter", ctypes.c_int32), ("proj", ctypes.c_void_p), ("w_gate", ctypes.c_void_p),
+                ("w_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p)]
 
 
 class MoeVerifyError(RuntimeError):
@@ -71,6 +77,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     L.moe_verify_profile.argtypes = [vp, ctypes.c_int]
     L.moe_verify_profile_read.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
     L.moe_verify_expert_counts.argtypes = [vp, ctypes.POINTER(ctypes.c_int32)]
+    L.moe_draft_init.argtypes = [vp, ctypes.POINTER(DraftWeightPtrs), vp]
+    L.moe_draft_step.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, vp]
     for name in EXPORTS:
         if name not in ("moe_verify_destroy", "moe_verify_last_error"):
             getattr(L, name).restype = ctypes.c_int
@@ -126,6 +134,20 @@ def upload_weights(weights, device="cuda") -> dict:
             "w_up": dev(weights.w_up), "w_down": dev(weights.w_down), "lm_head": dev(weights.lm_head)}
 
 
+def upload_draft_weights(dweights, device="cuda") -> dict:
+    """Copy host draft-block weights (workload.DraftWeights) to device tensors."""
+    import torch
+
+    def dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+        return torch.from_numpy(a).to(device)
+
+    return {"inter": int(dweights.inter), "proj": dev(dweights.proj), "w_gate": dev(dweights.w_gate),
+            "w_up": dev(dweights.w_up), "w_down": dev(dweights.w_down)}
+
+
 class MoeVerify:
     """A library context: repacked weights plus workspace for up to max_positions positions."""
 
@@ -147,6 +169,15 @@ class MoeVerify:
     def debug_layer(self, layer: int, x_in, T: int, moe_out=None, topk_id=None, topk_w=None, stream=None):
         _check(load_library().moe_verify_debug_layer(self._h, layer, _ptr(x_in), T, _ptr(moe_out), _ptr(topk_id),
                                                      _ptr(topk_w), _stream(stream)), "moe_verify_debug_layer")
+
+    def draft_init(self, dev_draft_weights: dict, stream=None):
+        w = DraftWeightPtrs(dev_draft_weights["inter"], *(_ptr(dev_draft_weights[k])
+                                                          for k in ("proj", "w_gate", "w_up", "w_down")))
+        _check(load_library().moe_draft_init(self._h, ctypes.byref(w), _stream(stream)), "moe_draft_init")
+
+    def draft_step(self, hidden, accepted_len, committed, B: int, Kv: int, K: int, drafts, stream=None):
+        _check(load_library().moe_draft_step(self._h, _ptr(hidden), _ptr(accepted_len), _ptr(committed), B, Kv, K,
+                                              _ptr(drafts), _stream(stream)), "moe_draft_step")
 
     def profile(self, enable: bool):
         _check(load_library().moe_verify_profile(self._h, int(enable)), "moe_verify_profile")

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB_DIR = os.path.join(PKG, "_lib")
 LIB_PATH = os.path.join(LIB_DIR, "libmoe_verify.so")
-SOURCES = ["kernels.hip", "tiled.hip", "api.hip"]
+SOURCES = ["kernels.hip", "tiled.hip", "draft.hip", "api.hip"]
 ARCH = os.environ.get("MOE_VERIFY_ARCH", "gfx950")
 
 

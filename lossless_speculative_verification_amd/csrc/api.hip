@@ -147,6 +147,19 @@ struct moe_verify_ctx {
   void* ybuf = nullptr;  // expert outputs, one row per slot, in the weight element type
   mv::Top2* part = nullptr;
   int32_t* counts = nullptr;  // [L][E] routed-slot count per expert, last step
+  // draft block (moe_draft_init): packed weights and its own buffers; the projection and
+  // block outputs use ybuf, the normalised rows a, the LM partials part, the GEMM work list
+  // work / n_work
+  int draft_inter = 0;
+  uint4* draft_proj_p = nullptr;  // H x 2H, pair layout
+  uint4* draft_up_p = nullptr;    // gate/up pairs, I_d x H
+  uint4* draft_down_p = nullptr;  // H x I_d
+  void* draft_u = nullptr;        // [P][2H] block input rows
+  float* draft_z = nullptr;       // [P][H] block residual stream (the next step's hidden state)
+  float* draft_zero = nullptr;    // [P][H] zeros (residual before the projection)
+  float* draft_ones = nullptr;    // [P] unit gates
+  void* draft_h = nullptr;        // [P][I_d] SwiGLU rows
+  int32_t* draft_ids = nullptr;   // [P] drafts of the current step
   std::vector<void*> allocs;
   // profiling: one event pair per launch of the last step, and running totals
   bool prof = false;
@@ -394,6 +407,39 @@ MV_API int moe_verify_init(const moe_verify_config* cfg, const moe_verify_weight
   return ok();
 }
 
+namespace {
+
+// LM head and argmax over the normalised rows c->a of Tn positions.
+int run_lm_head(moe_verify_ctx* c, int Tn, int32_t* argmax_out, float* margin_out, hipStream_t st) {
+  const moe_verify_config& g = c->cfg;
+  // Workgroups (kLmWaves wavefronts, one per CU) cover one row block of up to kLmRows
+  // positions; pairs per wavefront so that the workgroups of one row block make about
+  // one round on the device (further row blocks share the weight stream through L2).
+  const int n_items = (Tn + mv::kLmRows - 1) / mv::kLmRows;
+  const int target = c->n_cu * mv::kLmWaves;  // pair streams per round
+  const int ppw = std::max(1, (c->NQ_lm + target - 1) / target);
+  const int n_pg = (c->NQ_lm + mv::kLmWaves * ppw - 1) / (mv::kLmWaves * ppw);
+  mv::GemmArgs a{};
+  a.A = c->a;
+  a.B = c->lm_p;
+  a.K = g.hidden;
+  a.NQ = c->NQ_lm;
+  a.n_valid = g.vocab;
+  a.Tn = Tn;
+  a.part = c->part;
+  a.n_pg = n_pg;
+  a.lm_ppw = ppw;
+  c->prof_begin(MOE_PROF_LM_HEAD, st);
+  MV_CHECK(mv::launch_gemm(g.wdtype, mv::EPI_LM, a, (unsigned)(n_items * n_pg), st));
+  c->prof_end(st);
+  c->prof_begin(MOE_PROF_ARGMAX, st);
+  MV_CHECK(mv::launch_argmax_reduce(c->part, n_pg, Tn, argmax_out, margin_out, st));
+  c->prof_end(st);
+  return MOE_OK;
+}
+
+}  // namespace
+
 MV_API int moe_verify_step(moe_verify_ctx* c, const float* hidden_in, int32_t B, int32_t K, int32_t* argmax_out,
                            float* margin_out, float* hidden_out, void* stream) {
   if (!c) return fail(MOE_EINVAL, "context is NULL");
@@ -417,29 +463,8 @@ MV_API int moe_verify_step(moe_verify_ctx* c, const float* hidden_in, int32_t B,
                                  g.n_shared, g.n_routed, g.top_k, g.rms_eps, false, !use_tiled(g, Tn), st));
   c->prof_end(st);
   if (g.vocab > 0) {
-    // Workgroups (kLmWaves wavefronts, one per CU) cover one row block of up to kLmRows
-    // positions; pairs per wavefront so that the workgroups of one row block make about
-    // one round on the device (further row blocks share the weight stream through L2).
-    const int n_items = (Tn + mv::kLmRows - 1) / mv::kLmRows;
-    const int target = c->n_cu * mv::kLmWaves;  // pair streams per round
-    const int ppw = std::max(1, (c->NQ_lm + target - 1) / target);
-    const int n_pg = (c->NQ_lm + mv::kLmWaves * ppw - 1) / (mv::kLmWaves * ppw);
-    mv::GemmArgs a{};
-    a.A = c->a;
-    a.B = c->lm_p;
-    a.K = g.hidden;
-    a.NQ = c->NQ_lm;
-    a.n_valid = g.vocab;
-    a.Tn = Tn;
-    a.part = c->part;
-    a.n_pg = n_pg;
-    a.lm_ppw = ppw;
-    c->prof_begin(MOE_PROF_LM_HEAD, st);
-    MV_CHECK(mv::launch_gemm(g.wdtype, mv::EPI_LM, a, (unsigned)(n_items * n_pg), st));
-    c->prof_end(st);
-    c->prof_begin(MOE_PROF_ARGMAX, st);
-    MV_CHECK(mv::launch_argmax_reduce(c->part, n_pg, Tn, argmax_out, margin_out, st));
-    c->prof_end(st);
+    rc = run_lm_head(c, Tn, argmax_out, margin_out, st);
+    if (rc) return rc;
   }
   return ok();
 }
@@ -473,6 +498,112 @@ MV_API int moe_verify_debug_layer(moe_verify_ctx* c, int32_t layer, const float*
   const size_t kb = (size_t)T * g.top_k * 4;
   if (topk_id) MV_CHECK(hipMemcpyAsync(topk_id, c->topk_id, kb, hipMemcpyDeviceToDevice, st));
   if (topk_w) MV_CHECK(hipMemcpyAsync(topk_w, c->topk_w, kb, hipMemcpyDeviceToDevice, st));
+  return ok();
+}
+
+MV_API int moe_draft_init(moe_verify_ctx* c, const moe_draft_weights* w, void* stream) {
+  if (!c) return fail(MOE_EINVAL, "context is NULL");
+  if (!w) return fail(MOE_EINVAL, "weights is NULL");
+  const moe_verify_config& g = c->cfg;
+  if (g.vocab <= 0) return fail(MOE_EINVAL, "the draft block needs a context with an LM head (vocab > 0)");
+  if (!w->proj || !w->w_gate || !w->w_up || !w->w_down) return fail(MOE_EINVAL, "a required weight pointer is NULL");
+  if (!aligned16(w->proj) || !aligned16(w->w_gate) || !aligned16(w->w_up) || !aligned16(w->w_down))
+    return fail(MOE_EINVAL, "weight pointers must be 16-byte aligned");
+  const int H = g.hidden, Id = w->inter, es = c->es;
+  if (Id < 16 || Id > 16384 || Id % 16 != 0 || (Id * es) % mv::kRowBlockBytes != 0)
+    return fail(MOE_EUNSUPPORTED, "draft inter %d: need a multiple of %d in [16, 16384]", Id, mv::kRowBlockBytes / es);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  DeviceGuard dg(c->device);
+  if (dg.err != hipSuccess) return fail(MOE_EDEVICE, "device select: %s", hipGetErrorString(dg.err));
+  const size_t P = (size_t)g.max_positions;
+  const int NQ_h = (H + 31) / 32, NKB_2H = 2 * H * es / mv::kRowBlockBytes, NKB_I = Id * es / mv::kRowBlockBytes;
+  hipError_t ae = hipSuccess;
+  auto A = [&](auto** p, size_t bytes) {
+    if (ae == hipSuccess) ae = c->alloc(p, bytes);
+  };
+  A(&c->draft_proj_p, (size_t)NQ_h * NKB_2H * mv::kPairUnits * 16);
+  A(&c->draft_up_p, (size_t)(Id / 16) * c->NKB_H * mv::kPairUnits * 16);
+  A(&c->draft_down_p, (size_t)NQ_h * NKB_I * mv::kPairUnits * 16);
+  A(&c->draft_u, P * 2 * H * es);
+  A(&c->draft_z, P * H * sizeof(float));
+  A(&c->draft_zero, P * H * sizeof(float));
+  A(&c->draft_ones, P * sizeof(float));
+  A(&c->draft_h, (P + 1) * Id * es);
+  A(&c->draft_ids, P * sizeof(int32_t));
+  if (ae != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(MOE_ENOMEM, "device allocation failed: %s", hipGetErrorString(ae));
+  }
+  const int row_h = H * es;
+  MV_CHECK(mv::launch_repack_pairs(w->proj, w->proj, c->draft_proj_p, 1, H, 2 * row_h, NQ_h, NKB_2H, 0,
+                                   (size_t)H * 2 * row_h, st));
+  MV_CHECK(mv::launch_repack_pairs(w->w_gate, w->w_up, c->draft_up_p, 1, Id, row_h, Id / 16, c->NKB_H, 1,
+                                   (size_t)Id * row_h, st));
+  MV_CHECK(mv::launch_repack_pairs(w->w_down, w->w_down, c->draft_down_p, 1, H, Id * es, NQ_h, NKB_I, 0,
+                                   (size_t)H * Id * es, st));
+  MV_CHECK(hipMemsetAsync(c->draft_zero, 0, P * H * sizeof(float), st));
+  MV_CHECK(mv::launch_fill(c->draft_ones, P, 1.0f, st));
+  MV_CHECK(hipStreamSynchronize(st));
+  c->draft_inter = Id;
+  return ok();
+}
+
+MV_API int moe_draft_step(moe_verify_ctx* c, const float* hidden, const int32_t* accepted_len,
+                          const int32_t* committed, int32_t B, int32_t Kv, int32_t K, int32_t* drafts, void* stream) {
+  if (!c) return fail(MOE_EINVAL, "context is NULL");
+  if (c->draft_inter == 0) return fail(MOE_EINVAL, "no draft weights: call moe_draft_init first");
+  const moe_verify_config& g = c->cfg;
+  if (B < 1) return fail(MOE_EINVAL, "B = %d, need B >= 1", B);
+  if (Kv < 0) return fail(MOE_EINVAL, "Kv = %d, need Kv >= 0", Kv);
+  if (K < 1) return fail(MOE_EINVAL, "K = %d, need K >= 1", K);
+  if ((int64_t)B * (Kv + 1) > g.max_positions)
+    return fail(MOE_EINVAL, "B*(Kv+1) = %lld exceeds max_positions %d", (long long)B * (Kv + 1), g.max_positions);
+  if (!hidden || !accepted_len || !committed || !drafts) return fail(MOE_EINVAL, "a required pointer is NULL");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  DeviceGuard dg(c->device);
+  if (dg.err != hipSuccess) return fail(MOE_EDEVICE, "device select: %s", hipGetErrorString(dg.err));
+  const int H = g.hidden, Id = c->draft_inter, mb = mv::kGemmMB;
+  const int max_items = (g.max_positions + mb - 1) / mb;
+  // The GEMMs see one always-on expert (routed count 0) whose work items are row blocks.
+  mv::GemmArgs a{};
+  a.work = c->work;
+  a.n_work = c->n_work;
+  a.Tn = B;
+  a.k = 0; a.E = 0; a.KS = 1; a.H = H; a.I = Id;
+  a.max_items = max_items;
+  const int wave_target = c->n_cu * mv::kGemmWaves * MV_GEMM_WAVES_PER_SIMD;
+  const int items = (B + mb - 1) / mb;
+  auto grid = [&](int NQ, int wpg, int* ppw) {
+    *ppw = items * NQ >= wave_target ? 2 : 1;
+    return (unsigned)((max_items * ((NQ + *ppw - 1) / *ppw) + wpg - 1) / wpg);
+  };
+  MV_CHECK(mv::launch_draft_plan(c->work, c->n_work, B, mb, st));
+  for (int i = 0; i < K; ++i) {
+    MV_CHECK(mv::launch_draft_input(g.wdtype, hidden, accepted_len, committed, Kv, c->draft_z, c->draft_ids, drafts, K,
+                                    i, c->lm_p, c->NKB_H, H, g.vocab, g.rms_eps, c->draft_u, B, st));
+    // projection 2H -> H (an output-side GEMM like the experts' down projection)
+    mv::GemmArgs p = a;
+    p.A = c->draft_u; p.B = c->draft_proj_p; p.K = 2 * H; p.NQ = (H + 31) / 32; p.ybuf = c->ybuf;
+    unsigned n_wg = grid(p.NQ, mv::kStreamWavesDown, &p.ppw);
+    MV_CHECK(mv::launch_gemm(g.wdtype, mv::EPI_DOWN, p, n_wg, st));
+    // residual stream z = projection output; a = bf16(RMSNorm(z)) (one unit-gate slot per row)
+    MV_CHECK(mv::launch_norm_route(g.wdtype, false, c->draft_zero, c->ybuf, nullptr, c->draft_z, nullptr, c->a, nullptr,
+                                   nullptr, nullptr, c->draft_ones, B, H, 0, 0, 1, g.rms_eps, false, true, st));
+    mv::GemmArgs u = a;  // gate/up + SwiGLU
+    u.A = c->a; u.B = c->draft_up_p; u.K = H; u.NQ = Id / 16; u.h = c->draft_h;
+    n_wg = grid(u.NQ, mv::kStreamWavesUp, &u.ppw);
+    MV_CHECK(mv::launch_gemm(g.wdtype, mv::EPI_UP, u, n_wg, st));
+    mv::GemmArgs d = a;  // down
+    d.A = c->draft_h; d.B = c->draft_down_p; d.K = Id; d.NQ = (H + 31) / 32; d.ybuf = c->ybuf;
+    n_wg = grid(d.NQ, mv::kStreamWavesDown, &d.ppw);
+    MV_CHECK(mv::launch_gemm(g.wdtype, mv::EPI_DOWN, d, n_wg, st));
+    // z <- z + block output; a = bf16(RMSNorm(z)) for the LM head
+    MV_CHECK(mv::launch_norm_route(g.wdtype, false, c->draft_z, c->ybuf, nullptr, c->draft_z, nullptr, c->a, nullptr,
+                                   nullptr, nullptr, c->draft_ones, B, H, 0, 0, 1, g.rms_eps, false, true, st));
+    const int rc = run_lm_head(c, B, c->draft_ids, nullptr, st);
+    if (rc) return rc;
+  }
+  MV_CHECK(mv::launch_draft_store(c->draft_ids, drafts, B, K, st));
   return ok();
 }
 

@@ -99,4 +99,19 @@ hipError_t launch_accept(const int32_t* drafts, const int32_t* argmax, int B, in
 hipError_t launch_combine(int wdtype, const void* ybuf, const int32_t* slot_row, const float* gate, int Tn, int H,
                           int k, int S, bool pos_major, float* m, hipStream_t stream);
 
+// Draft block (draft.hip). Input rows of draft step `step` for B sequences (one
+// workgroup each): U[b] = [RMSNorm(h_b), RMSNorm(E[t_b])] in the weight type, with h_b, t_b
+// the verifier pass's last accepted row (step 0) or the previous step's output hidden
+// state and draft (step > 0, which also stores drafts[b][step-1]); E = the LM head in its
+// pair layout (NKB K blocks per pair). H <= 4096.
+hipError_t launch_draft_input(int wdtype, const float* hidden, const int32_t* accepted, const int32_t* committed,
+                              int Kv, const float* z_prev, const int32_t* ids_prev, int32_t* drafts, int K, int step,
+                              const void* lm, int NKB, int H, int V, float eps, void* U, int B, hipStream_t stream);
+// Work list of ceil(B / mb) row blocks of one always-on expert (expert index 0).
+hipError_t launch_draft_plan(int4* work, int32_t* n_work, int B, int mb, hipStream_t stream);
+// drafts[b][K-1] = ids[b].
+hipError_t launch_draft_store(const int32_t* ids, int32_t* drafts, int B, int K, hipStream_t stream);
+// p[0..n) = v.
+hipError_t launch_fill(float* p, size_t n, float v, hipStream_t stream);
+
 }  // namespace mv

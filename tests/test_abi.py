@@ -132,6 +132,11 @@ def test_entry_points_reject_before_any_device_call(lib):
     assert lib.accept_greedy(16, None, 1, 3, 16, 16, None) == bnd.MOE_EINVAL
     assert lib.accept_greedy(16, 16, 1, 3, None, 16, None) == bnd.MOE_EINVAL
     assert "NULL" in bnd.last_error()
+    # draft block: null context / weights
+    dw = bnd.DraftWeightPtrs(128, 16, 16, 16, 16)
+    assert lib.moe_draft_init(None, ctypes.byref(dw), None) == bnd.MOE_EINVAL
+    assert lib.moe_draft_step(None, 16, 16, 16, 1, 3, 3, 16, None) == bnd.MOE_EINVAL
+    assert "NULL" in bnd.last_error()
     lib.moe_verify_destroy(None)  # no-op
 
 
