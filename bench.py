@@ -161,6 +161,124 @@ def sweep(args):
     ctx.close()
 
 
+def draft_bench(args):
+    """Cost of the draft block and of the closed loop, on the 12-block decode model.
+
+    One draft step streams the block's projection and SwiGLU weights and the LM head;
+    with random weights its drafts are meaningless, so only time and bytes are reported.
+    The loop step is one verifier pass (B=32, K=3) + acceptance + K=3 draft steps, the
+    drafts feeding the next pass, captured in one HIP graph.
+    """
+    import torch
+
+    from lossless_speculative_verification_amd import binding as bnd
+    from lossless_speculative_verification_amd import workload as W
+
+    wl = W.WORKLOADS["decode_b32_k3"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("[draft] generating weights")
+    dw_h = W.make_draft_weights(wl)
+    dw = bnd.upload_weights(W.make_weights(wl), dev)
+    ctx = bnd.MoeVerify(wl, dw)
+    del dw
+    ctx.draft_init(bnd.upload_draft_weights(dw_h, dev))
+    torch.cuda.empty_cache()
+    B, K, T, H = wl.batch, wl.drafts, wl.positions, wl.hidden
+    x = torch.from_numpy(W.make_hidden(wl)).to(dev)
+    ids = torch.empty(T, dtype=torch.int32, device=dev)
+    hout = torch.empty_like(x)
+    n_acc = torch.empty(B, dtype=torch.int32, device=dev)
+    com = torch.empty(B, K + 1, dtype=torch.int32, device=dev)
+    drafts = torch.zeros(B, K, dtype=torch.int32, device=dev)
+
+    def draft():
+        ctx.draft_step(hout, n_acc, com, B, K, K, drafts)
+
+    def loop():
+        ctx.step(x, B, K, ids, None, hout)
+        bnd.accept_greedy(drafts, ids, B, K, n_acc, com)
+        draft()
+
+    loop()
+    torch.cuda.synchronize()
+    graphs = {}
+    for name, fn in (("draft", draft), ("loop", loop)):
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            fn()
+        graphs[name] = g
+    ms_draft = _time(graphs["draft"].replay, args.steps, args.warmup)
+    ms_loop = _time(graphs["loop"].replay, args.steps, args.warmup)
+    w = 2 if wl.wdtype == "bf16" else 4
+    per_step = (H * 2 * H + 3 * H * dw_h.inter + wl.vocab * H) * w + B * H * w
+    line = {"bench": "draft_block", "workload": wl.name, "B": B, "K": K, "draft_inter": dw_h.inter,
+            "ms_draft": round(ms_draft, 4), "draft_bytes": K * per_step,
+            "draft_hbm_gbs": round(K * per_step / (ms_draft * 1e-3) / 1e9, 1),
+            "draft_hbm_frac": round(K * per_step / (ms_draft * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "ms_loop": round(ms_loop, 4), "loop_positions_per_s": round(T / (ms_loop * 1e-3), 1), "mode": "hip_graph"}
+    print(json.dumps(line), flush=True)
+    ctx.close()
+
+
+def mixed_bench(args):
+    """One page's prefill (1,156 visual-token positions) and a B=32, K=3 verify in one pass
+    (one stream of the expert weights for both) against the two passes run one after the
+    other, on the 12-block decode model."""
+    import torch
+
+    from lossless_speculative_verification_amd import binding as bnd
+    from lossless_speculative_verification_amd import workload as W
+
+    wl = W.WORKLOADS["decode_b32_k3"]
+    n_pre, B, K = 1156, wl.batch, wl.drafts
+    Tv = B * (K + 1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("[mixed] generating weights")
+    dw = bnd.upload_weights(W.make_weights(wl), dev)
+    ctx = bnd.MoeVerify(wl, dw, n_pre + Tv)
+    del dw
+    torch.cuda.empty_cache()
+    x = torch.from_numpy(W.make_hidden(wl, n_pre + Tv)).to(dev)
+    ids = torch.empty(Tv, dtype=torch.int32, device=dev)
+    first = torch.empty(1, dtype=torch.int32, device=dev)  # the page's first token
+
+    def mixed():
+        ctx.step_mixed(x, n_pre, B, K, ids)
+
+    def separate():
+        ctx.step_mixed(x[: n_pre + 1], n_pre, 1, 0, first)  # prefill pass: LM head on its last position
+        ctx.step(x[n_pre:], B, K, ids)
+
+    res = {}
+    for name, fn in (("mixed", mixed), ("separate", separate)):
+        fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            fn()
+        res[name] = _time(g.replay, args.steps, args.warmup)
+    line = {"bench": "mixed_pass", "workload": wl.name, "n_prefill": n_pre, "B": B, "K": K,
+            "ms_mixed": round(res["mixed"], 4), "ms_separate": round(res["separate"], 4),
+            "speedup": round(res["separate"] / res["mixed"], 3),
+            "positions_per_s_mixed": round((n_pre + Tv) / (res["mixed"] * 1e-3), 1), "mode": "hip_graph"}
+    print(json.dumps(line), flush=True)
+    ctx.close()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -172,6 +290,12 @@ def main():
     ap.add_argument("--sweep", action="store_true",
                     help="time the 12-block decode model over K in {0,1,3} x B in {1,4,32}, HIP graph and eager "
                          "(one JSON line per point instead of the bench line)")
+    ap.add_argument("--draft", action="store_true",
+                    help="time the draft block (K steps after a B=32, K=3 pass of the 12-block model) and the "
+                         "closed verify + accept + draft loop (one JSON line instead of the bench line)")
+    ap.add_argument("--mixed", action="store_true",
+                    help="time a mixed pass (one 1,156-token page prefill + a B=32, K=3 verify) against the two "
+                         "passes run separately, 12-block model (one JSON line instead of the bench line)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 256 MiB device to device (scale reference for the HBM byte counters)")
     args = ap.parse_args()
@@ -193,6 +317,12 @@ def main():
 
     if args.sweep:
         sweep(args)
+        return
+    if args.draft:
+        draft_bench(args)
+        return
+    if args.mixed:
+        mixed_bench(args)
         return
 
     import torch
@@ -350,6 +480,8 @@ def main():
         "kernels_us": {k: round(v["avg_us"], 2) for k, v in per_kind.items()},
         "touched_experts_per_block": acc["touched_per_block"],
     }
+    if wl.n_biased > 0:  # share of the routed slots that land on the biased ("hot") experts
+        out["hot_slot_frac"] = round(float(counts[:, : wl.n_biased].sum() / max(counts.sum(), 1)), 4)
     print(json.dumps(out), flush=True)
     ctx.close()
 

@@ -120,6 +120,21 @@ int moe_verify_init(const moe_verify_config *cfg, const moe_verify_weights *weig
 int moe_verify_step(moe_verify_ctx *ctx, const float *hidden_in, int32_t B, int32_t K,
                     int32_t *argmax_out, float *margin_out, float *hidden_out, void *stream);
 
+/* A mixed pass: n_prefill prompt positions (e.g. the visual tokens of a new page) and
+ * B*(K+1) verify positions go through the MoE blocks together, so one stream of the
+ * expert weights serves both (a serving engine's mixed batch); the LM head and argmax run
+ * on the verify positions only.
+ *   hidden_in  [n_prefill + B*(K+1)][H] float32 device: prefill rows first, then the
+ *              verify rows b*(K+1)+j (required);
+ *   argmax_out [B*(K+1)] int32 device, margin_out [B*(K+1)] float32 device or NULL: as
+ *              for moe_verify_step, for the verify rows;
+ *   hidden_out [n_prefill + B*(K+1)][H] float32 device or NULL (required iff vocab == 0).
+ * n_prefill >= 0 and n_prefill + B*(K+1) <= max_positions; otherwise as moe_verify_step
+ * (n_prefill = 0 is exactly moe_verify_step). */
+int moe_verify_step_mixed(moe_verify_ctx *ctx, const float *hidden_in, int32_t n_prefill, int32_t B,
+                          int32_t K, int32_t *argmax_out, float *margin_out, float *hidden_out,
+                          void *stream);
+
 /* Greedy acceptance for B sequences of K drafts.
  *   draft_ids    [B][K] int32 device (ids outside [0, V) simply never match);
  *   argmax_ids   [B][K+1] int32 device (the step's argmax_out);

@@ -409,8 +409,8 @@ MV_API int moe_verify_init(const moe_verify_config* cfg, const moe_verify_weight
 
 namespace {
 
-// LM head and argmax over the normalised rows c->a of Tn positions.
-int run_lm_head(moe_verify_ctx* c, int Tn, int32_t* argmax_out, float* margin_out, hipStream_t st) {
+// LM head and argmax over the normalised rows row0 .. row0 + Tn - 1 of c->a.
+int run_lm_head(moe_verify_ctx* c, int row0, int Tn, int32_t* argmax_out, float* margin_out, hipStream_t st) {
   const moe_verify_config& g = c->cfg;
   // Workgroups (kLmWaves wavefronts, one per CU) cover one row block of up to kLmRows
   // positions; pairs per wavefront so that the workgroups of one row block make about
@@ -420,7 +420,7 @@ int run_lm_head(moe_verify_ctx* c, int Tn, int32_t* argmax_out, float* margin_ou
   const int ppw = std::max(1, (c->NQ_lm + target - 1) / target);
   const int n_pg = (c->NQ_lm + mv::kLmWaves * ppw - 1) / (mv::kLmWaves * ppw);
   mv::GemmArgs a{};
-  a.A = c->a;
+  a.A = static_cast<const char*>(c->a) + (size_t)row0 * g.hidden * c->es;
   a.B = c->lm_p;
   a.K = g.hidden;
   a.NQ = c->NQ_lm;
@@ -440,14 +440,15 @@ int run_lm_head(moe_verify_ctx* c, int Tn, int32_t* argmax_out, float* margin_ou
 
 }  // namespace
 
-MV_API int moe_verify_step(moe_verify_ctx* c, const float* hidden_in, int32_t B, int32_t K, int32_t* argmax_out,
-                           float* margin_out, float* hidden_out, void* stream) {
-  if (!c) return fail(MOE_EINVAL, "context is NULL");
-  int rc = check_step(&c->cfg, B, K, hidden_in != nullptr, argmax_out != nullptr, hidden_out != nullptr);
-  if (rc) return rc;
+namespace {
+
+// The MoE blocks over Tn = n_prefill + Tv positions, the final norm, and the LM head and
+// argmax over the last Tv of them.
+int run_pass(moe_verify_ctx* c, const float* hidden_in, int n_prefill, int Tv, int32_t* argmax_out, float* margin_out,
+             float* hidden_out, hipStream_t st) {
   const moe_verify_config& g = c->cfg;
-  const int Tn = B * (K + 1);
-  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int Tn = n_prefill + Tv;
+  int rc;
   DeviceGuard dg(c->device);
   if (dg.err != hipSuccess) return fail(MOE_EDEVICE, "device select: %s", hipGetErrorString(dg.err));
   c->n_pairs = 0;
@@ -463,10 +464,37 @@ MV_API int moe_verify_step(moe_verify_ctx* c, const float* hidden_in, int32_t B,
                                  g.n_shared, g.n_routed, g.top_k, g.rms_eps, false, !use_tiled(g, Tn), st));
   c->prof_end(st);
   if (g.vocab > 0) {
-    rc = run_lm_head(c, Tn, argmax_out, margin_out, st);
+    rc = run_lm_head(c, n_prefill, Tv, argmax_out, margin_out, st);
     if (rc) return rc;
   }
-  return ok();
+  return MOE_OK;
+}
+
+}  // namespace
+
+MV_API int moe_verify_step(moe_verify_ctx* c, const float* hidden_in, int32_t B, int32_t K, int32_t* argmax_out,
+                           float* margin_out, float* hidden_out, void* stream) {
+  if (!c) return fail(MOE_EINVAL, "context is NULL");
+  const int rc = check_step(&c->cfg, B, K, hidden_in != nullptr, argmax_out != nullptr, hidden_out != nullptr);
+  if (rc) return rc;
+  const int rp = run_pass(c, hidden_in, 0, B * (K + 1), argmax_out, margin_out, hidden_out,
+                          static_cast<hipStream_t>(stream));
+  return rp ? rp : ok();
+}
+
+MV_API int moe_verify_step_mixed(moe_verify_ctx* c, const float* hidden_in, int32_t n_prefill, int32_t B, int32_t K,
+                                 int32_t* argmax_out, float* margin_out, float* hidden_out, void* stream) {
+  if (!c) return fail(MOE_EINVAL, "context is NULL");
+  if (n_prefill < 0) return fail(MOE_EINVAL, "n_prefill = %d, need n_prefill >= 0", n_prefill);
+  const moe_verify_config& g = c->cfg;
+  int rc = check_step(&g, B, K, hidden_in != nullptr, argmax_out != nullptr, hidden_out != nullptr);
+  if (rc) return rc;
+  if ((int64_t)n_prefill + (int64_t)B * (K + 1) > g.max_positions)
+    return fail(MOE_EINVAL, "n_prefill + B*(K+1) = %lld exceeds max_positions %d",
+                (long long)n_prefill + (long long)B * (K + 1), g.max_positions);
+  rc = run_pass(c, hidden_in, n_prefill, B * (K + 1), argmax_out, margin_out, hidden_out,
+                static_cast<hipStream_t>(stream));
+  return rc ? rc : ok();
 }
 
 MV_API int accept_greedy(const int32_t* draft_ids, const int32_t* argmax_ids, int32_t B, int32_t K,
@@ -600,7 +628,7 @@ MV_API int moe_draft_step(moe_verify_ctx* c, const float* hidden, const int32_t*
     // z <- z + block output; a = bf16(RMSNorm(z)) for the LM head
     MV_CHECK(mv::launch_norm_route(g.wdtype, false, c->draft_z, c->ybuf, nullptr, c->draft_z, nullptr, c->a, nullptr,
                                    nullptr, nullptr, c->draft_ones, B, H, 0, 0, 1, g.rms_eps, false, true, st));
-    const int rc = run_lm_head(c, B, c->draft_ids, nullptr, st);
+    const int rc = run_lm_head(c, 0, B, c->draft_ids, nullptr, st);
     if (rc) return rc;
   }
   MV_CHECK(mv::launch_draft_store(c->draft_ids, drafts, B, K, st));
