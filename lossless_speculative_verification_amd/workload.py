@@ -84,6 +84,11 @@ WORKLOADS = {
     # 12 layers + LM head, B=128, K=3, router bias +3.0 on experts 0..7, p=0.8.
     "skewed_b128_k3": Workload("skewed_b128_k3", 1280, 64, 6, 2, 896, 12, 129280, "bf16", 128, 3, 0.8, 1004,
                                bias_value=3.0, n_biased=8),
+    # Same shape with bias +1.367 on experts 0..7: about 70% of the routed slots land on them
+    # (the share the skewed stress case asks for; +3.0 puts nearly all there), while every
+    # expert still gets some.
+    "skewed70_b128_k3": Workload("skewed70_b128_k3", 1280, 64, 6, 2, 896, 12, 129280, "bf16", 128, 3, 0.8, 1004,
+                                 bias_value=1.367, n_biased=8),
 }
 
 

@@ -147,3 +147,42 @@ def test_device_loop_with_draft_block_equals_greedy():
     spec, sp = run(K)
     assert spec == greedy
     log(f"[draft] device loop: {sp} passes with the draft block vs {gp} greedy")
+
+
+def test_draft_step_graph_replay_matches_eager():
+    """The draft step captured in a HIP graph reproduces the eager drafts on every replay,
+    with eager work and synchronisations between replays."""
+    wl = W.WORKLOADS["layer1_bf16"].with_(batch=8, drafts=3)
+    dw = W.make_draft_weights(wl, DRAFT_INTER["layer1_bf16"])
+    c = _ctx_with_draft(wl, dw, wl.positions)
+    B, Kv, K, T = 8, 3, 3, wl.positions
+    x = torch.from_numpy(W.make_hidden(wl)).to(DEV)
+    ids = torch.empty(T, dtype=torch.int32, device=DEV)
+    hout = torch.empty_like(x)
+    n = torch.empty(B, dtype=torch.int32, device=DEV)
+    com = torch.empty(B, Kv + 1, dtype=torch.int32, device=DEV)
+    d_in = torch.zeros(B, Kv, dtype=torch.int32, device=DEV)
+    out = torch.empty(B, K, dtype=torch.int32, device=DEV)
+    c.step(x, B, Kv, ids, None, hout)
+    bnd.accept_greedy(d_in, ids, B, Kv, n, com)
+    c.draft_step(hout, n, com, B, Kv, K, out)
+    torch.cuda.synchronize()
+    ref = out.clone()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        c.draft_step(hout, n, com, B, Kv, K, out)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    log("[draft] graph capture")
+    with torch.cuda.graph(g):
+        c.draft_step(hout, n, com, B, Kv, K, out)
+    for i in range(3):
+        out.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {i} differs"
+        c.step(x, B, Kv, ids, None, hout)  # eager work between replays (same inputs)
+        torch.cuda.synchronize()

@@ -233,8 +233,9 @@ def test_decode_deterministic_and_batch_invariant():
 # ----------------------------------------------------------------------------- skewed routing
 
 
-def test_skewed_step_sampled():
-    wl = WL["skewed_b128_k3"]
+@pytest.mark.parametrize("name", ["skewed_b128_k3", "skewed70_b128_k3"])
+def test_skewed_step_sampled(name):
+    wl = WL[name]
     x = W.make_hidden(wl)
     seqs = np.random.default_rng(5).choice(wl.batch, 16, replace=False)
     rows = tuple(int(s * (wl.drafts + 1) + j) for s in sorted(seqs) for j in range(wl.drafts + 1))

@@ -493,3 +493,22 @@ def test_speculative_with_the_draft_block_equals_greedy():
     greedy = O.greedy_decode(nt, [2, 9], 24)
     spec, passes = O.speculative_decode(nt, draft, [2, 9], 24, 3)
     assert spec == greedy and passes <= 24
+
+
+# ----------------------------------------------------------------------------- skewed routing
+
+
+@pytest.mark.parametrize("name,lo,hi", [("skewed_b128_k3", 0.99, 1.0), ("skewed70_b128_k3", 0.66, 0.74)])
+def test_router_bias_hot_share(name, lo, hi):
+    """Share of the routed slots on the 8 biased experts in the first block, from the
+    oracle's own routing of the seeded hidden states: the bias +3.0 is three router-logit
+    standard deviations (sqrt(1280) * 0.02 = 0.72 for unit-RMS inputs) and takes nearly all
+    slots; +1.367 takes about 70 %."""
+    wl = W.WORKLOADS[name]
+    wts = W.make_weights(wl, layers=range(1), lm_head=False)
+    x = W.make_hidden(wl)
+    a = O.round_bf16(O.rms_norm(x, wl.rms_eps))
+    r = O.router_logits(a, O.as_f64(wts.router[0], wl.wdtype), wts.router_bias[0])
+    ids, _ = O.select_topk(r, wl.top_k)
+    share = float((ids < wl.n_biased).mean())
+    assert lo <= share <= hi, share
