@@ -186,3 +186,35 @@ def test_draft_step_graph_replay_matches_eager():
         assert torch.equal(out, ref), f"replay {i} differs"
         c.step(x, B, Kv, ids, None, hout)  # eager work between replays (same inputs)
         torch.cuda.synchronize()
+
+
+def test_draft_step_decode_size():
+    """The bench's configuration: a B=32, K=3 pass of the 12-block model, then 3 draft
+    steps for all 32 sequences, against the oracle's chain. Through 12 blocks few
+    sequences keep every routing gap above the gate on their whole accepted path (one of
+    the 32 here), so exact comparison covers those; the accepted lengths and the drafts
+    must be in range everywhere."""
+    wl = W.WORKLOADS["decode_b32_k3"]
+    B, Kv, K = wl.batch, wl.drafts, 3
+    wts = host_weights(wl)
+    dw = W.make_draft_weights(wl)
+    x = W.make_hidden(wl)
+    log("[draft] decode size")
+    c = _ctx_with_draft(wl, dw, wl.positions)
+    ref_ids = O.verify_step(wl, wts, x)["ids"]
+    drafts_in = W.make_drafts(wl, ref_ids)
+    ids, n, drafts = _gpu_chain(c, x, drafts_in, B, Kv, K)
+    ref, n_ref, dr, decisive = _oracle_chain(wl, wts, dw, x, drafts_in, B, Kv, K)
+    checked = 0
+    for b in range(B):
+        if not decisive[b, : n_ref[b] + 1].all():
+            continue
+        assert n[b] == n_ref[b]
+        for i in range(K):
+            if dr["margin"][b, i] <= GATE:
+                break
+            assert drafts[b, i] == dr["drafts"][b, i], (b, i)
+            checked += 1
+    log(f"[draft] {checked} decisive drafts compared")
+    assert checked >= 1
+    assert ((n >= 0) & (n <= Kv)).all() and ((drafts >= 0) & (drafts < wl.vocab)).all()

@@ -69,3 +69,37 @@ def test_mixed_pass_rejects_oversize():
     with pytest.raises(bnd.MoeVerifyError) as ei:
         c.step_mixed(xd, -1, 2, 3, ids)
     assert ei.value.code == bnd.MOE_EINVAL
+
+
+def test_mixed_pass_bench_size_sampled():
+    """The bench's mixed pass: one page of 1,156 prefill positions and a B=32, K=3 verify
+    through the 12-block model; the oracle follows 48 sampled prefill rows and every verify
+    row."""
+    wl = W.WORKLOADS["decode_b32_k3"]
+    n_pre, B, K = 1156, wl.batch, wl.drafts
+    Tv = B * (K + 1)
+    wts = host_weights(wl)
+    x = W.make_hidden(wl, n_pre + Tv)
+    log("[mixed] bench size, sampled rows")
+    c = context(wl, n_pre + Tv)
+    xd = torch.from_numpy(x).to(DEV)
+    ids = torch.empty(Tv, dtype=torch.int32, device=DEV)
+    hout = torch.empty_like(xd)
+    c.step_mixed(xd, n_pre, B, K, ids, None, hout)
+    torch.cuda.synchronize()
+    ids, hout = ids.cpu().numpy(), hout.cpu().numpy()
+    rng = np.random.default_rng(12)
+    # 12 blocks: about a fifth of the positions have every routing gap (and the LM margin)
+    # above the gate, so the comparison runs on those rows
+    pre = np.array(sorted(rng.choice(n_pre, 48, replace=False).tolist()))
+    ref_pre = O.verify_step(wl.with_(vocab=0), wts, x[pre])
+    dp = decisive_positions(ref_pre)
+    assert dp.sum() >= 2, dp.sum()
+    assert end_to_end_rel_err(hout[pre][dp], ref_pre["hidden_out"][dp], x[pre][dp], wl.n_layers) < TOL[wl.wdtype]
+    vrows = np.arange(Tv)
+    ref = O.verify_step(wl, wts, x[n_pre + vrows])
+    dec = decisive_positions(ref)
+    assert dec.sum() >= 4, dec.sum()
+    assert np.array_equal(ids[dec], ref["ids"][dec])
+    assert end_to_end_rel_err(hout[n_pre + vrows][dec], ref["hidden_out"][dec], x[n_pre + vrows][dec],
+                              wl.n_layers) < TOL[wl.wdtype]
