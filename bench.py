@@ -286,6 +286,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode_b32_k3")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a HIP graph")
+    ap.add_argument("--flush-mall", action="store_true",
+                    help="overwrite 1 GiB between timed steps (each step timed alone) so no weight is still in "
+                         "the 256 MB memory-side cache when a step starts")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true",
                     help="time the 12-block decode model over K in {0,1,3} x B in {1,4,32}, HIP graph and eager "
@@ -394,12 +397,27 @@ def main():
         run()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(args.steps):
-        run()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+    if args.flush_mall:
+        # each step timed on its own, after 1 GiB of writes has evicted the weights from the
+        # memory-side cache; the timed region holds the step only
+        scrub = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        total = 0.0
+        for i in range(args.steps):
+            scrub.fill_(float(i))
+            e0.record()
+            run()
+            e1.record()
+            torch.cuda.synchronize()
+            total += e0.elapsed_time(e1)
+        ms = total / args.steps
+        del scrub
+    else:
+        e0.record()
+        for _ in range(args.steps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
 
     # eager timing for reference (launch overhead visible)
     for _ in range(3):
@@ -468,7 +486,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.wdtype, "data": "synthetic",
         "config": {"workload": wl.name, "B": B, "K": K, "blocks": wl.n_layers, "hidden": wl.hidden,
                    "routed_experts": wl.n_routed, "top_k": wl.top_k, "shared_experts": wl.n_shared,
-                   "inter": wl.inter, "vocab": wl.vocab, "positions": T, "mode": mode},
+                   "inter": wl.inter, "vocab": wl.vocab, "positions": T, "mode": mode,
+                   "mall_flushed": bool(args.flush_mall)},
         "roofline": roof,
         "step_roofline": {"bound": "hbm", "achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                           "frac": round(step_gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": acc["step_bytes"],
