@@ -185,8 +185,9 @@ typedef struct {
 /* Attach draft-block weights to a context that has an LM head (vocab > 0): copy them
  * into the library's layout on `stream`, allocate the block's workspace for
  * max_positions sequences, and wait. Calling it again replaces the weights (buffers of
- * earlier calls are freed by moe_verify_destroy). MOE_EINVAL for a context without an
- * LM head or a NULL pointer, MOE_EUNSUPPORTED for an inter outside the limits. */
+ * earlier calls are freed by moe_verify_destroy); if that call fails after its argument
+ * checks, the context is left without a draft block. MOE_EINVAL for a context without
+ * an LM head or a NULL pointer, MOE_EUNSUPPORTED for an inter outside the limits. */
 int moe_draft_init(moe_verify_ctx *ctx, const moe_draft_weights *weights, void *stream);
 
 /* K draft steps for B sequences right after a verifier pass of Kv drafts:

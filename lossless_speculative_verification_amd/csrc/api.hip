@@ -543,6 +543,8 @@ MV_API int moe_draft_init(moe_verify_ctx* c, const moe_draft_weights* w, void* s
   hipStream_t st = static_cast<hipStream_t>(stream);
   DeviceGuard dg(c->device);
   if (dg.err != hipSuccess) return fail(MOE_EDEVICE, "device select: %s", hipGetErrorString(dg.err));
+  // detached until the new weights are in place: a failure below leaves no draft block
+  c->draft_inter = 0;
   const size_t P = (size_t)g.max_positions;
   const int NQ_h = (H + 31) / 32, NKB_2H = 2 * H * es / mv::kRowBlockBytes, NKB_I = Id * es / mv::kRowBlockBytes;
   hipError_t ae = hipSuccess;
