@@ -218,3 +218,28 @@ def test_draft_step_decode_size():
     log(f"[draft] {checked} decisive drafts compared")
     assert checked >= 1
     assert ((n >= 0) & (n <= Kv)).all() and ((drafts >= 0) & (drafts < wl.vocab)).all()
+
+
+def test_draft_step_argument_errors():
+    """Host-side checks of moe_draft_step and moe_draft_init on a live context."""
+    wl = W.WORKLOADS["tiny_fp32"]
+    c = context(wl)
+    B = 1
+    h = torch.zeros(4, wl.hidden, device=DEV)
+    n = torch.zeros(B, dtype=torch.int32, device=DEV)
+    com = torch.zeros(B, 4, dtype=torch.int32, device=DEV)
+    out = torch.empty(B, 3, dtype=torch.int32, device=DEV)
+    dw = W.make_draft_weights(wl, DRAFT_INTER["tiny_fp32"])
+    c.draft_init(bnd.upload_draft_weights(dw, DEV))
+    for args in ((h, n, com, B, 3, 0, out),             # K = 0
+                 (h, n, com, 0, 3, 3, out),             # B = 0
+                 (h, n, com, B, -1, 3, out),            # Kv < 0
+                 (h, n, com, c.cfg.max_positions + 1, 0, 3, out)):  # too many rows
+        with pytest.raises(bnd.MoeVerifyError) as ei:
+            c.draft_step(*args)
+        assert ei.value.code == bnd.MOE_EINVAL
+    bad = bnd.upload_draft_weights(dw, DEV)
+    bad["inter"] = 48  # not a multiple of 64 float32 elements
+    with pytest.raises(bnd.MoeVerifyError) as ei:
+        c.draft_init(bad)
+    assert ei.value.code == bnd.MOE_EUNSUPPORTED
