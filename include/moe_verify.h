@@ -26,8 +26,12 @@
  * to the lower expert index, gates renormalised over the k selected; bias-free
  * SwiGLU experts down(silu(gate x) * up x); shared experts always on with weight 1;
  * a final RMSNorm before the LM head; argmax ties to the lower vocabulary index.
- * With bf16 weights, bf16 is materialised at the RMSNorm outputs and the SwiGLU
- * output; accumulation, the residual stream, gates and logits are float32.
+ * Numerics with bf16 weights: every product takes bf16 activations (the RMSNorm
+ * outputs and the SwiGLU output) and accumulates in float32. Each expert's output is
+ * stored in bf16 before the gate-weighted sum, a rounding of at most 2^-9 of each
+ * element, well inside the library's 2e-2 relative tolerance on a block's output; the
+ * definition it is checked against keeps that output exact. The residual stream, router
+ * logits, gates, the gated sum and the LM-head logits are float32.
  *
  * Conventions for every call:
  *   - Pointers named "device" are HIP device pointers; structs are host memory.
@@ -68,7 +72,9 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
  *   0 <= n_shared <= 8, n_layers >= 1, vocab >= 0,
  *   hidden and inter multiples of 128 (bf16) or 64 (f32), and hidden a multiple of 256
  *   (bf16) or 128 (f32) when vocab > 0; hidden <= 4096 (bf16) or 2048 (f32),
- *   inter <= 16384, max_positions >= 1. */
+ *   inter <= 16384, max_positions >= 1; and when bf16 weights can take the tiled expert
+ *   GEMM (hidden and inter >= 256, max_positions >= 256), its operands must stay below
+ *   4 GiB: max_positions*hidden*2 and (max_positions*(top_k+n_shared)+1)*inter*2 bytes. */
 typedef struct {
   int32_t hidden;        /* H                                                        */
   int32_t n_routed;      /* E routed experts                                         */
@@ -160,6 +166,27 @@ const char *moe_verify_last_error(void);
 int moe_verify_debug_layer(moe_verify_ctx *ctx, int32_t layer, const float *x_in, int32_t T,
                            float *moe_out, int32_t *topk_id, float *topk_w, void *stream);
 
+/* Test hook: the final RMSNorm, the LM head and the argmax alone, on a caller-supplied
+ * residual stream x_in [T][H] float32 device (e.g. a reference pass's hidden state after
+ * its last block), 1 <= T <= max_positions: argmax_out [T] int32 device (required) and
+ * margin_out [T] float32 device or NULL, computed exactly as moe_verify_step computes
+ * them from its own last block ("jina-ocr-v1" model page, summary paragraph: the
+ * verifier's greedy choice). MOE_EINVAL for a context without an LM head. */
+int moe_verify_debug_head(moe_verify_ctx *ctx, const float *x_in, int32_t T, int32_t *argmax_out,
+                          float *margin_out, void *stream);
+
+/* Test hook: the routing plan of the last MoE block the context ran (the last block of the
+ * last moe_verify_step or moe_verify_step_mixed, or the block of the last
+ * moe_verify_debug_layer), over that pass's T positions (architecture paragraph: top-6 of
+ * 64 routed experts; the plan groups each expert's rows for its expert GEMM):
+ *   row_slot [T*k] int32 device out (required): the routed slot t*k + j held by each row of
+ *            the expert-major order, in which expert e's rows follow expert e-1's and hold
+ *            its slots in ascending slot order (a stable sort of the slots by expert);
+ *   counts   [E] int32 device out, or NULL: the routed-slot count of each expert.
+ * Row r belongs to expert e when counts[0] + ... + counts[e-1] <= r < counts[0] + ... +
+ * counts[e]. MOE_EINVAL if no block has run on the context. */
+int moe_verify_debug_plan(moe_verify_ctx *ctx, int32_t *row_slot, int32_t *counts, void *stream);
+
 /* ---- draft block: drafts the next pass's K tokens on the device ---------------------- */
 
 /* The draft block is a multi-token-prediction head ("jina-ocr-v1" model page, FastMTP
@@ -184,9 +211,9 @@ typedef struct {
 
 /* Attach draft-block weights to a context that has an LM head (vocab > 0): copy them
  * into the library's layout on `stream`, allocate the block's workspace for
- * max_positions sequences, and wait. Calling it again replaces the weights (buffers of
- * earlier calls are freed by moe_verify_destroy); if that call fails after its argument
- * checks, the context is left without a draft block. MOE_EINVAL for a context without
+ * max_positions sequences, and wait. Calling it again replaces the weights: it waits for
+ * `stream`, frees the earlier call's buffers, then allocates and copies anew; if that call
+ * fails after its argument checks, the context is left without a draft block. MOE_EINVAL for a context without
  * an LM head or a NULL pointer, MOE_EUNSUPPORTED for an inter outside the limits. */
 int moe_draft_init(moe_verify_ctx *ctx, const moe_draft_weights *weights, void *stream);
 

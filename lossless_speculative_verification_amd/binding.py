@@ -20,7 +20,7 @@ MOE_F32, MOE_BF16 = 0, 1
 EXPORTS = ("moe_verify_check_config", "moe_verify_check_step", "moe_verify_init", "moe_verify_step",
            "accept_greedy", "moe_verify_destroy", "moe_verify_last_error", "moe_verify_debug_layer",
            "moe_verify_profile", "moe_verify_profile_read", "moe_verify_expert_counts", "moe_draft_init",
-           "moe_draft_step", "moe_verify_step_mixed")
+           "moe_draft_step", "moe_verify_step_mixed", "moe_verify_debug_head", "moe_verify_debug_plan")
 PROF_KINDS = ("norm_route", "plan", "gemm_up", "gemm_down", "lm_head", "argmax")
 
 
@@ -53,13 +53,12 @@ _lib = None
 def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     """Load libmoe_verify.so (once) and declare the C signatures.
 
-    The path defaults to the in-tree build, or to $MOE_VERIFY_LIB when that is set
-    (another build of the same sources, e.g. with different GEMM shape knobs).
+    The path defaults to the in-tree build.
     """
     global _lib
     if _lib is not None:
         return _lib
-    path = path or os.environ.get("MOE_VERIFY_LIB") or LIB_PATH
+    path = path or LIB_PATH
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with `python -m lossless_speculative_verification_amd.build`")
     L = ctypes.CDLL(path)
@@ -80,6 +79,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     L.moe_draft_init.argtypes = [vp, ctypes.POINTER(DraftWeightPtrs), vp]
     L.moe_verify_step_mixed.argtypes = [vp, vp, i32, i32, i32, vp, f32p, f32p, vp]
     L.moe_draft_step.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, vp]
+    L.moe_verify_debug_head.argtypes = [vp, vp, i32, vp, f32p, vp]
+    L.moe_verify_debug_plan.argtypes = [vp, vp, vp, vp]
     for name in EXPORTS:
         if name not in ("moe_verify_destroy", "moe_verify_last_error"):
             getattr(L, name).restype = ctypes.c_int
@@ -176,6 +177,14 @@ class MoeVerify:
     def debug_layer(self, layer: int, x_in, T: int, moe_out=None, topk_id=None, topk_w=None, stream=None):
         _check(load_library().moe_verify_debug_layer(self._h, layer, _ptr(x_in), T, _ptr(moe_out), _ptr(topk_id),
                                                      _ptr(topk_w), _stream(stream)), "moe_verify_debug_layer")
+
+    def debug_head(self, x_in, T: int, argmax_out, margin_out=None, stream=None):
+        _check(load_library().moe_verify_debug_head(self._h, _ptr(x_in), T, _ptr(argmax_out), _ptr(margin_out),
+                                                    _stream(stream)), "moe_verify_debug_head")
+
+    def debug_plan(self, row_slot, counts=None, stream=None):
+        _check(load_library().moe_verify_debug_plan(self._h, _ptr(row_slot), _ptr(counts), _stream(stream)),
+               "moe_verify_debug_plan")
 
     def draft_init(self, dev_draft_weights: dict, stream=None):
         w = DraftWeightPtrs(dev_draft_weights["inter"], *(_ptr(dev_draft_weights[k])

@@ -85,6 +85,16 @@ int check_config(const moe_verify_config* c) {
                 c->wdtype == MOE_BF16 ? 4096 : 2048, c->inter);
   if (max_work_items(*c, c->max_positions) > 65535 || (int64_t)c->max_positions * c->top_k > (1ll << 30))
     return fail(MOE_EUNSUPPORTED, "max_positions %d too large", c->max_positions);
+  // The tiled expert GEMM forms each lane's activation offset in 32 bits: its operand
+  // buffers (the normalised rows a [P][H] and the SwiGLU rows h [P*(k+S)+1][I]) must stay
+  // below 4 GiB whenever a pass can take that path.
+  if (c->wdtype == MOE_BF16 && c->hidden >= 256 && c->inter >= 256 && c->max_positions >= MV_TILED_MIN_POSITIONS) {
+    const int64_t P = c->max_positions, KS = c->top_k + c->n_shared;
+    const int64_t a_bytes = P * c->hidden * 2, h_bytes = (P * KS + 1) * c->inter * 2;
+    if (a_bytes >= (1ll << 32) || h_bytes >= (1ll << 32))
+      return fail(MOE_EUNSUPPORTED, "max_positions %d: the expert GEMM operands (%lld and %lld bytes) must stay below 4 GiB",
+                  c->max_positions, (long long)a_bytes, (long long)h_bytes);
+  }
   return MOE_OK;
 }
 
@@ -147,6 +157,7 @@ struct moe_verify_ctx {
   void* ybuf = nullptr;  // expert outputs, one row per slot, in the weight element type
   mv::Top2* part = nullptr;
   int32_t* counts = nullptr;  // [L][E] routed-slot count per expert, last step
+  int last_T = 0, last_layer = 0;  // positions and block of the last MoE block run (debug_plan)
   // draft block (moe_draft_init): packed weights and its own buffers; the projection and
   // block outputs use ybuf, the normalised rows a, the LM partials part, the GEMM work list
   // work / n_work
@@ -184,6 +195,18 @@ struct moe_verify_ctx {
     (void)hipEventRecord(ev[2 * n_pairs + 1], st);
     ++n_pairs;
   }
+  // Free one allocation made by alloc() (waits for the device first) and clear the pointer.
+  template <typename P>
+  void release(P** p) {
+    if (!*p) return;
+    for (size_t i = 0; i < allocs.size(); ++i)
+      if (allocs[i] == static_cast<void*>(*p)) {
+        (void)hipFree(allocs[i]);
+        allocs.erase(allocs.begin() + i);
+        break;
+      }
+    *p = nullptr;
+  }
   template <typename P>
   hipError_t alloc(P** out, size_t bytes) {
     void* p = nullptr;
@@ -212,6 +235,8 @@ int run_block(moe_verify_ctx* c, int l, const float* x_in, const void* ybuf_prev
   const int E = g.n_routed, S = g.n_shared, k = g.top_k, KS = k + S, H = g.hidden, I = g.inter;
   const bool tiled = use_tiled(g, Tn);
   const int mb = tiled ? mv::kTileM : mv::kGemmMB;
+  c->last_T = Tn;
+  c->last_layer = l;
   const int wmax = (int)max_work_items(g, Tn, mb);
   mv::PlanArgs pa{};
   pa.topk_id = c->topk_id;
@@ -529,6 +554,41 @@ MV_API int moe_verify_debug_layer(moe_verify_ctx* c, int32_t layer, const float*
   return ok();
 }
 
+MV_API int moe_verify_debug_head(moe_verify_ctx* c, const float* x_in, int32_t T, int32_t* argmax_out,
+                                 float* margin_out, void* stream) {
+  if (!c) return fail(MOE_EINVAL, "context is NULL");
+  const moe_verify_config& g = c->cfg;
+  if (g.vocab <= 0) return fail(MOE_EINVAL, "the context has no LM head (vocab == 0)");
+  if (T < 1 || T > g.max_positions) return fail(MOE_EINVAL, "T = %d out of range [1, %d]", T, g.max_positions);
+  if (!x_in || !argmax_out) return fail(MOE_EINVAL, "x_in and argmax_out are required");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  DeviceGuard dg(c->device);
+  if (dg.err != hipSuccess) return fail(MOE_EDEVICE, "device select: %s", hipGetErrorString(dg.err));
+  // the final norm with no expert outputs to add: a = RMSNorm(x_in) in the weight type
+  c->prof_begin(MOE_PROF_NORM_ROUTE, st);
+  MV_CHECK(mv::launch_norm_route(g.wdtype, false, x_in, nullptr, nullptr, nullptr, nullptr, c->a, nullptr, nullptr,
+                                 nullptr, nullptr, T, g.hidden, g.n_shared, g.n_routed, g.top_k, g.rms_eps, false,
+                                 true, st));
+  c->prof_end(st);
+  const int rc = run_lm_head(c, 0, T, argmax_out, margin_out, st);
+  return rc ? rc : ok();
+}
+
+MV_API int moe_verify_debug_plan(moe_verify_ctx* c, int32_t* row_slot, int32_t* counts, void* stream) {
+  if (!c) return fail(MOE_EINVAL, "context is NULL");
+  if (!row_slot) return fail(MOE_EINVAL, "row_slot is NULL");
+  if (c->last_T < 1) return fail(MOE_EINVAL, "no MoE block has run on this context");
+  const moe_verify_config& g = c->cfg;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  DeviceGuard dg(c->device);
+  if (dg.err != hipSuccess) return fail(MOE_EDEVICE, "device select: %s", hipGetErrorString(dg.err));
+  MV_CHECK(mv::launch_row_slot(c->row_dst, c->last_T * g.top_k, g.top_k, g.top_k + g.n_shared, row_slot, st));
+  if (counts)
+    MV_CHECK(hipMemcpyAsync(counts, c->counts + (size_t)c->last_layer * g.n_routed, (size_t)g.n_routed * sizeof(int32_t),
+                            hipMemcpyDeviceToDevice, st));
+  return ok();
+}
+
 MV_API int moe_draft_init(moe_verify_ctx* c, const moe_draft_weights* w, void* stream) {
   if (!c) return fail(MOE_EINVAL, "context is NULL");
   if (!w) return fail(MOE_EINVAL, "weights is NULL");
@@ -543,8 +603,19 @@ MV_API int moe_draft_init(moe_verify_ctx* c, const moe_draft_weights* w, void* s
   hipStream_t st = static_cast<hipStream_t>(stream);
   DeviceGuard dg(c->device);
   if (dg.err != hipSuccess) return fail(MOE_EDEVICE, "device select: %s", hipGetErrorString(dg.err));
-  // detached until the new weights are in place: a failure below leaves no draft block
+  // detached until the new weights are in place: a failure below leaves no draft block.
+  // A previous call's buffers are freed first (hipFree waits for work still using them).
   c->draft_inter = 0;
+  MV_CHECK(hipStreamSynchronize(st));
+  c->release(&c->draft_proj_p);
+  c->release(&c->draft_up_p);
+  c->release(&c->draft_down_p);
+  c->release(&c->draft_u);
+  c->release(&c->draft_z);
+  c->release(&c->draft_zero);
+  c->release(&c->draft_ones);
+  c->release(&c->draft_h);
+  c->release(&c->draft_ids);
   const size_t P = (size_t)g.max_positions;
   const int NQ_h = (H + 31) / 32, NKB_2H = 2 * H * es / mv::kRowBlockBytes, NKB_I = Id * es / mv::kRowBlockBytes;
   hipError_t ae = hipSuccess;

@@ -1251,6 +1251,14 @@ __global__ void k_combine(const T* __restrict__ ybuf, const int32_t* __restrict_
   }
 }
 
+// Routed slot of each expert-major row, from the row's position-major expert-output row.
+__global__ void k_row_slot(const int32_t* __restrict__ row_dst, int n, int k, int KS, int32_t* __restrict__ out) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= n) return;
+  const int d = row_dst[r];
+  out[r] = (d / KS) * k + d % KS;
+}
+
 // ============================================================================ launchers
 
 static unsigned grid_for(size_t n, unsigned block, unsigned cap = 65535u * 8u) {
@@ -1417,6 +1425,11 @@ hipError_t launch_argmax_reduce(const Top2* part, int n_pg, int Tn, int32_t* arg
 hipError_t launch_accept(const int32_t* drafts, const int32_t* argmax, int B, int K, int32_t* accepted,
                          int32_t* committed, hipStream_t stream) {
   k_accept<<<(B + 255) / 256, 256, 0, stream>>>(drafts, argmax, B, K, accepted, committed);
+  return hipGetLastError();
+}
+
+hipError_t launch_row_slot(const int32_t* row_dst, int n, int k, int KS, int32_t* row_slot, hipStream_t stream) {
+  k_row_slot<<<(n + 255) / 256, 256, 0, stream>>>(row_dst, n, k, KS, row_slot);
   return hipGetLastError();
 }
 

@@ -99,6 +99,10 @@ hipError_t launch_accept(const int32_t* drafts, const int32_t* argmax, int B, in
 hipError_t launch_combine(int wdtype, const void* ybuf, const int32_t* slot_row, const float* gate, int Tn, int H,
                           int k, int S, bool pos_major, float* m, hipStream_t stream);
 
+// Test hook: row_slot[r] = slot t*k + j of routed row r, from its position-major
+// expert-output row row_dst[r] = t*KS + j (n = T*k rows).
+hipError_t launch_row_slot(const int32_t* row_dst, int n, int k, int KS, int32_t* row_slot, hipStream_t stream);
+
 // Draft block (draft.hip). Input rows of draft step `step` for B sequences (one
 // workgroup each): U[b] = [RMSNorm(h_b), RMSNorm(E[t_b])] in the weight type, with h_b, t_b
 // the verifier pass's last accepted row (step 0) or the previous step's output hidden

@@ -32,11 +32,13 @@ the design notes):
 6. each expert is a bias-free SwiGLU: down(silu(gate x) * up x);
 7. blocks are pre-norm: x <- x + MoE(RMSNorm(x)), RMSNorm with gamma 1 and eps
    inside the square root, and a final RMSNorm before the LM head;
-8. for bf16 weights, bf16 is materialised at the RMSNorm output (the input of the
-   router, the experts and the LM head), at the SwiGLU output and at each expert's
-   output (the down projection's result, before its gate), as a BF16 checkpoint run
-   under Transformers or vLLM produces them; the residual stream is float32;
-   everything else is exact (float64 here);
+8. for bf16 weights (bf16 weights with float32 accumulation), bf16 is materialised
+   at the activation input of every matrix product: the RMSNorm output (the input of
+   the router, the experts and the LM head) and the SwiGLU output (the input of the
+   down projection). Products are accumulated exactly (float64 here) and their
+   results are kept unrounded: router logits, each expert's output (the down
+   projection's result, before its gate), the gated sum and the logits; the
+   residual stream is float32;
 9. acceptance: the longest prefix of drafts equal to the verifier's argmax at the
    matching positions is accepted, and the verifier's token after it is added;
 10. the draft block (the pages name FastMTP, a multi-token-prediction head that drafts
@@ -47,8 +49,9 @@ the design notes):
    embedding), projects 2H -> H (bias-free), adds a pre-norm dense SwiGLU block with
    a residual, applies the final RMSNorm and the shared LM head, and drafts the
    greedy token; its hidden state and token feed step i + 1. bf16 is materialised
-   as in reading 8: the two normalised halves, the projection output, the block's
-   normalised input, its SwiGLU product and its output, and the LM-head input.
+   as in reading 8, at the inputs of the products: the two normalised halves, the
+   block's normalised input, its SwiGLU product and the LM-head input; the projection
+   output and the block's output are float32 like the verifier's residual stream.
 """
 from __future__ import annotations
 
@@ -136,17 +139,16 @@ def silu(z) -> np.ndarray:
     return z / (1.0 + np.exp(-z))
 
 
-def expert_ffn(a_rows, w_gate, w_up, w_down, round_bf16_io: bool) -> np.ndarray:
+def expert_ffn(a_rows, w_gate, w_up, w_down, round_bf16_h: bool) -> np.ndarray:
     """One SwiGLU expert on a set of positions (reading 6): (silu(a Wg^T) * (a Wu^T)) Wd^T.
 
-    With round_bf16_io (bf16 weights, reading 8) the SwiGLU product and the expert's
-    output are rounded to bf16.
+    With round_bf16_h (bf16 weights, reading 8) the SwiGLU product, the input of the
+    down projection, is rounded to bf16; the expert's output is exact.
     """
     h = silu(a_rows @ w_gate.T) * (a_rows @ w_up.T)
-    if round_bf16_io:
+    if round_bf16_h:
         h = round_bf16(h)
-    y = h @ w_down.T
-    return round_bf16(y) if round_bf16_io else y
+    return h @ w_down.T
 
 
 def moe_layer(cfg, weights, layer: int, x) -> dict:
@@ -336,7 +338,7 @@ def draft_step(cfg, weights, dweights, h, tok, K: int) -> dict:
     for i in range(K):
         emb = as_f64(weights.lm_head[tok], cfg.wdtype)
         u = np.concatenate([rnd(rms_norm(h, cfg.rms_eps)), rnd(rms_norm(emb, cfg.rms_eps))], axis=1)
-        x = rnd(u @ wp.T).astype(np.float32)               # projection output, the block's residual
+        x = (u @ wp.T).astype(np.float32)                  # projection output, the block's residual
         a = rnd(rms_norm(x, cfg.rms_eps))
         y = expert_ffn(a, wg, wu, wd, bf)                   # the same SwiGLU form as an expert
         x = (x.astype(np.float64) + y).astype(np.float32)

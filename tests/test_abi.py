@@ -84,6 +84,20 @@ def test_bad_configs_rejected(lib, kw, code):
     assert bnd.last_error() != ""
 
 
+def test_expert_gemm_operands_below_4gib(lib):
+    """The tiled expert GEMM forms per-lane activation offsets in 32 bits: configs whose
+    SwiGLU rows (max_positions*(top_k+n_shared)+1)*inter*2 bytes or normalised rows
+    max_positions*hidden*2 bytes reach 2^32 are refused; the float32 path never tiles."""
+    big = dict(hidden=1280, n_routed=64, top_k=6, n_shared=2, inter=16384, n_layers=1, vocab=0,
+               wdtype=bnd.MOE_BF16)
+    # (P*8 + 1) * 16384 * 2 < 2^32  <=>  P <= 16383
+    assert lib.moe_verify_check_config(ctypes.byref(_cfg(**big, max_positions=16383))) == bnd.MOE_OK
+    assert lib.moe_verify_check_config(ctypes.byref(_cfg(**big, max_positions=16384))) == bnd.MOE_EUNSUPPORTED
+    assert "4 GiB" in bnd.last_error()
+    f32 = dict(big, inter=2048, hidden=2048, wdtype=bnd.MOE_F32)
+    assert lib.moe_verify_check_config(ctypes.byref(_cfg(**f32, max_positions=140000))) == bnd.MOE_OK
+
+
 def test_null_config_rejected(lib):
     assert lib.moe_verify_check_config(None) == bnd.MOE_EINVAL
 
@@ -126,6 +140,8 @@ def test_entry_points_reject_before_any_device_call(lib):
     assert lib.moe_verify_step(None, 16, 1, 3, 16, None, None, None) == bnd.MOE_EINVAL
     assert lib.moe_verify_debug_layer(None, 0, 16, 4, None, None, None, None) == bnd.MOE_EINVAL
     assert lib.moe_verify_step_mixed(None, 16, 8, 1, 3, 16, None, None, None) == bnd.MOE_EINVAL
+    assert lib.moe_verify_debug_head(None, 16, 4, 16, None, None) == bnd.MOE_EINVAL
+    assert lib.moe_verify_debug_plan(None, 16, None, None) == bnd.MOE_EINVAL
     # acceptance
     assert lib.accept_greedy(16, 16, 0, 3, 16, 16, None) == bnd.MOE_EINVAL
     assert lib.accept_greedy(16, 16, 1, -1, 16, 16, None) == bnd.MOE_EINVAL

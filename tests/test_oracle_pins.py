@@ -163,9 +163,10 @@ def test_two_shared_experts_equal_one_concatenated():
     np.testing.assert_allclose(two, one, rtol=1e-12, atol=1e-12)
 
 
-def _dense_reference_layer(cfg, wts, x):
+def _dense_reference_layer(cfg, wts, x, layer=0):
     """Independent dense formulation in torch: every expert on every position,
-    top-k sets by brute force, gates from the full softmax renormalised."""
+    top-k sets by brute force, gates from the full softmax renormalised; bf16 at the
+    activation inputs of the products (normalised rows, SwiGLU output) only."""
     E, S, k = cfg.n_routed, cfg.n_shared, cfg.top_k
     f64 = lambda w: torch.from_numpy(O.as_f64(w, cfg.wdtype))
     xt = torch.from_numpy(np.asarray(x, np.float64))
@@ -174,9 +175,9 @@ def _dense_reference_layer(cfg, wts, x):
         a = u.float().to(torch.bfloat16).double()
     else:
         a = u
-    r = a @ f64(wts.router[0]).T
+    r = a @ f64(wts.router[layer]).T
     if wts.router_bias is not None:
-        r = r + torch.from_numpy(wts.router_bias[0]).double()
+        r = r + torch.from_numpy(wts.router_bias[layer]).double()
     p = torch.softmax(r, dim=1)
     G = torch.zeros_like(p)
     for t in range(x.shape[0]):
@@ -184,14 +185,30 @@ def _dense_reference_layer(cfg, wts, x):
         G[t, sel] = p[t, sel] / p[t, sel].sum()
     m = torch.zeros_like(xt)
     for e in range(E + S):
-        h = torch.nn.functional.silu(a @ f64(wts.w_gate[0, e]).T) * (a @ f64(wts.w_up[0, e]).T)
+        h = torch.nn.functional.silu(a @ f64(wts.w_gate[layer, e]).T) * (a @ f64(wts.w_up[layer, e]).T)
         if cfg.wdtype == "bf16":
             h = h.float().to(torch.bfloat16).double()
-        y = h @ f64(wts.w_down[0, e]).T
-        if cfg.wdtype == "bf16":
-            y = y.float().to(torch.bfloat16).double()
+        y = h @ f64(wts.w_down[layer, e]).T
         m += (G[:, e:e + 1] if e < E else 1.0) * y
     return m.numpy()
+
+
+def _dense_reference_pass(cfg, wts, x):
+    """Independent torch loop over the blocks: x <- float32(x + m_l) with m_l from the
+    dense layer above, then the final RMSNorm (bf16-rounded for bf16 weights) and the
+    greedy id, its margin over the runner-up, from the full logit matrix."""
+    import torch.nn.functional as F
+
+    x = np.asarray(x, np.float32)
+    for layer in range(cfg.n_layers):
+        m = _dense_reference_layer(cfg, wts, x, layer)
+        x = (torch.from_numpy(x).double() + torch.from_numpy(m)).float().numpy()
+    u = F.rms_norm(torch.from_numpy(x).double(), (cfg.hidden,), eps=cfg.rms_eps)
+    a = u.float().to(torch.bfloat16).double() if cfg.wdtype == "bf16" else u
+    logits = a @ torch.from_numpy(O.as_f64(wts.lm_head, cfg.wdtype)).T
+    ids = torch.argmax(logits, dim=1)  # first maximal index
+    top = torch.topk(logits, 2, dim=1).values
+    return x, ids.numpy(), (top[:, 0] - top[:, 1]).numpy()
 
 
 @pytest.mark.parametrize("wdtype", ["f32", "bf16"])
@@ -209,6 +226,51 @@ def test_moe_layer_matches_dense_formulation(wdtype, biased):
     err = np.abs(out["m"] - ref).max() / np.abs(ref).max()
     assert err < tol, err
     np.testing.assert_array_equal(out["x_next"], (x.astype(np.float64) + out["m"]).astype(np.float32))
+
+
+@pytest.mark.parametrize("n_layers", [2, 3])
+@pytest.mark.parametrize("wdtype", ["f32", "bf16"])
+@pytest.mark.parametrize("biased", [False, True])
+def test_verify_step_blocks_match_dense_loop(n_layers, wdtype, biased):
+    """The stacked pass (architecture paragraph: a decoder of several MoE layers): the
+    oracle's verify_step against an independent torch loop, block by block with a
+    float32 residual, then the final norm and a full-logit argmax. A block fed the wrong
+    residual, a layer's weights or bias taken from another block, or a final norm
+    without its bf16 rounding all change hidden_out, ids or margins here."""
+    cfg = Cfg(hidden=32, n_routed=8, top_k=3, n_shared=2, inter=12, n_layers=n_layers, vocab=50, wdtype=wdtype)
+    bias = None
+    if biased:  # a different bias per block, so a block reading another's fails
+        bias = np.random.default_rng(40 + n_layers).standard_normal((n_layers, 8)).astype(np.float32) * 0.8
+    wts = _rand_weights(cfg, 20 + n_layers, bias=bias)
+    x = np.random.default_rng(30 + n_layers).standard_normal((40, 32)).astype(np.float32)
+    out = O.verify_step(cfg, wts, x)
+    hx, ids, margin = _dense_reference_pass(cfg, wts, x)
+    # same float32 residual adds of float64 block outputs: equal up to the last float32 bit
+    rel = np.abs(out["hidden_out"].astype(np.float64) - hx).max() / np.abs(hx).max()
+    assert rel < 1e-6, rel
+    np.testing.assert_array_equal(out["ids"], ids)
+    np.testing.assert_allclose(out["margin"], margin, rtol=0, atol=1e-9)
+    # and the per-block records compose: each block's output is hidden_out's increment
+    xs = x.astype(np.float32)
+    for lay in out["layers"]:
+        xs = (xs.astype(np.float64) + lay["m"]).astype(np.float32)
+    np.testing.assert_array_equal(xs, out["hidden_out"])
+    # the pass is deeper than one block: dropping the last block changes the result
+    short = O.verify_step(cfg, wts, x, layers=n_layers - 1)
+    assert not np.array_equal(short["hidden_out"], out["hidden_out"])
+
+
+def test_final_norm_bf16_is_the_rounded_rms_norm():
+    """The final norm of a bf16 model rounds torch's RMSNorm to bf16 (reading 8); the
+    float32 model keeps it unrounded."""
+    import torch.nn.functional as F
+
+    x = np.random.default_rng(17).standard_normal((9, 64)).astype(np.float32) * 3.0
+    ref = F.rms_norm(torch.from_numpy(x).double(), (64,), eps=1e-6)
+    cb, cf = Cfg(wdtype="bf16"), Cfg(wdtype="f32")
+    np.testing.assert_array_equal(O.final_norm(cb, x), ref.float().to(torch.bfloat16).double().numpy())
+    np.testing.assert_allclose(O.final_norm(cf, x), ref.numpy(), rtol=1e-13, atol=0)
+    assert not np.array_equal(O.final_norm(cb, x), O.final_norm(cf, x))
 
 
 def test_moe_layer_closed_forms():
