@@ -279,83 +279,34 @@ def mixed_bench(args):
     ctx.close()
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="decode_b32_k3")
-    ap.add_argument("--eager", action="store_true", help="time eager launches instead of a HIP graph")
-    ap.add_argument("--flush-mall", action="store_true",
-                    help="overwrite 1 GiB between timed steps (each step timed alone) so no weight is still in "
-                         "the 256 MB memory-side cache when a step starts")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--sweep", action="store_true",
-                    help="time the 12-block decode model over K in {0,1,3} x B in {1,4,32}, HIP graph and eager "
-                         "(one JSON line per point instead of the bench line)")
-    ap.add_argument("--draft", action="store_true",
-                    help="time the draft block (K steps after a B=32, K=3 pass of the 12-block model) and the "
-                         "closed verify + accept + draft loop (one JSON line instead of the bench line)")
-    ap.add_argument("--mixed", action="store_true",
-                    help="time a mixed pass (one 1,156-token page prefill + a B=32, K=3 verify) against the two "
-                         "passes run separately, 12-block model (one JSON line instead of the bench line)")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="only copy 256 MiB device to device (scale reference for the HBM byte counters)")
-    args = ap.parse_args()
-    if args.copy_calibration:
-        import torch
+def expected_committed(wl):
+    """Expected tokens a pass commits per sequence when each draft equals the verifier's
+    choice with probability p independently: sum_{i=0..K} p^i (the bonus token, then each
+    further token needs one more agreeing draft)."""
+    return sum(wl.p_match ** i for i in range(wl.drafts + 1))
 
-        n = 256 << 20
-        src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes": n, "launches": 3}))
-        return
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the verify step is "
-              "data-parallel over sequences with no exchange, see the design notes.", file=sys.stderr)
-        sys.exit(2)
 
-    if args.sweep:
-        sweep(args)
-        return
-    if args.draft:
-        draft_bench(args)
-        return
-    if args.mixed:
-        mixed_bench(args)
-        return
+def timed_pass(ctx, wl, x, args):
+    """Time one step (verifier pass + acceptance) of wl on resident inputs x.
 
+    Drafts agree with the verifier's greedy choice with probability p; they are built from
+    one untimed pass's argmax (the verifier's own choices, as a drafter would see them).
+    The step is captured in a HIP graph (unless --eager) whose replays must reproduce the
+    eager result exactly, then timed over args.steps replays after args.warmup.
+    """
     import torch
 
     from lossless_speculative_verification_amd import binding as bnd
     from lossless_speculative_verification_amd import workload as W
 
-    wl = W.WORKLOADS[args.workload]
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    log(f"[bench] {wl.name}: generating weights")
-    t0 = time.perf_counter()
-    weights = W.make_weights(wl)
-    x_h = W.make_hidden(wl)
-    log(f"[bench] generated in {time.perf_counter() - t0:.1f} s; uploading + repacking")
-    dw = bnd.upload_weights(weights, dev)
-    ctx = bnd.MoeVerify(wl, dw)
-    del dw
-    torch.cuda.empty_cache()
-
+    dev = x.device
     T, B, K = wl.positions, wl.batch, wl.drafts
-    x = torch.from_numpy(x_h).to(dev)
     ids = torch.empty(T, dtype=torch.int32, device=dev)
     margin = torch.empty(T, dtype=torch.float32, device=dev)
     n_acc = torch.zeros(B, dtype=torch.int32, device=dev)
     committed = torch.empty(B, K + 1, dtype=torch.int32, device=dev)
     hidden_out = torch.empty_like(x) if wl.vocab == 0 else None
 
-    # Drafts that agree with the verifier's greedy choice with probability p: built from
-    # one untimed pass's argmax (the verifier's own choices, as a drafter would see them).
     ctx.step(x, B, K, ids if wl.vocab else None, margin if wl.vocab else None, hidden_out)
     torch.cuda.synchronize()
     counts = ctx.expert_counts()
@@ -429,6 +380,83 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     ms_eager = e0.elapsed_time(e1) / args.steps
+    com = int(n_acc.sum().item()) + B if wl.vocab else 0
+    return {"ms": ms, "ms_eager": ms_eager, "counts": counts, "mode": mode, "committed": com, "ids": ids,
+            "margin": margin, "hidden_out": hidden_out}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode_b32_k3")
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of a HIP graph")
+    ap.add_argument("--flush-mall", action="store_true",
+                    help="overwrite 1 GiB between timed steps (each step timed alone) so no weight is still in "
+                         "the 256 MB memory-side cache when a step starts")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time the 12-block decode model over K in {0,1,3} x B in {1,4,32}, HIP graph and eager "
+                         "(one JSON line per point instead of the bench line)")
+    ap.add_argument("--draft", action="store_true",
+                    help="time the draft block (K steps after a B=32, K=3 pass of the 12-block model) and the "
+                         "closed verify + accept + draft loop (one JSON line instead of the bench line)")
+    ap.add_argument("--mixed", action="store_true",
+                    help="time a mixed pass (one 1,156-token page prefill + a B=32, K=3 verify) against the two "
+                         "passes run separately, 12-block model (one JSON line instead of the bench line)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only copy 256 MiB device to device (scale reference for the HBM byte counters)")
+    args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+
+        n = 256 << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "launches": 3}))
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the verify step is "
+              "data-parallel over sequences with no exchange, see the design notes.", file=sys.stderr)
+        sys.exit(2)
+
+    if args.sweep:
+        sweep(args)
+        return
+    if args.draft:
+        draft_bench(args)
+        return
+    if args.mixed:
+        mixed_bench(args)
+        return
+
+    import torch
+
+    from lossless_speculative_verification_amd import binding as bnd
+    from lossless_speculative_verification_amd import workload as W
+
+    wl = W.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[bench] {wl.name}: generating weights")
+    t0 = time.perf_counter()
+    weights = W.make_weights(wl)
+    x_h = W.make_hidden(wl)
+    log(f"[bench] generated in {time.perf_counter() - t0:.1f} s; uploading + repacking")
+    dw = bnd.upload_weights(weights, dev)
+    ctx = bnd.MoeVerify(wl, dw)
+    del dw
+    torch.cuda.empty_cache()
+
+    x = torch.from_numpy(x_h).to(dev)
+    r = timed_pass(ctx, wl, x, args)
+    ms, ms_eager, counts, mode = r["ms"], r["ms_eager"], r["counts"], r["mode"]
+    T, B, K = wl.positions, wl.batch, wl.drafts
+    ids, margin, hidden_out = r["ids"], r["margin"], r["hidden_out"]
 
     # per-kernel durations from HIP events the library records around each launch
     ctx.profile(True)
@@ -438,7 +466,7 @@ def main():
     ctx.profile(False)
 
     acc = algorithmic(wl, counts)
-    committed_per_step = int(n_acc.sum().item()) + B if wl.vocab else 0
+    committed_per_step = r["committed"]
     per_kind = {k: {"avg_us": 1000.0 * v[0] / max(v[1], 1), "launches_per_step": v[1] / args.steps}
                 for k, v in prof.items()}
     up_us = per_kind["gemm_up"]["avg_us"]
@@ -501,6 +529,23 @@ def main():
     }
     if wl.n_biased > 0:  # share of the routed slots that land on the biased ("hot") experts
         out["hot_slot_frac"] = round(float(counts[:, : wl.n_biased].sum() / max(counts.sum(), 1)), 4)
+    if wl.vocab:
+        # the sampled value rides on one seeded draft draw; the expectation over draft draws
+        # at the same step time is B * sum_{i=0..K} p^i tokens per step
+        out["value_expected"] = round(B * expected_committed(wl) / (ms * 1e-3), 1)
+        out["committed_per_step_expected"] = round(B * expected_committed(wl), 2)
+    if wl.name == "decode_b32_k3" and not args.flush_mall:
+        # the K = 1 operating point of the same model and weights (the pages' best K with graphs)
+        wl1 = W.WORKLOADS["decode_b32_k1"]
+        log("[bench] K = 1 operating point")
+        r1 = timed_pass(ctx, wl1, torch.from_numpy(W.make_hidden(wl1)).to(dev), args)
+        acc1 = algorithmic(wl1, r1["counts"])
+        out["k1"] = {"workload": wl1.name, "B": wl1.batch, "K": wl1.drafts, "positions": wl1.positions,
+                     "ms_per_step": round(r1["ms"], 4),
+                     "value": round(r1["committed"] / (r1["ms"] * 1e-3), 1),
+                     "value_expected": round(wl1.batch * expected_committed(wl1) / (r1["ms"] * 1e-3), 1),
+                     "committed_per_step": r1["committed"],
+                     "step_hbm_frac": round(acc1["step_bytes"] / (r1["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     print(json.dumps(out), flush=True)
     ctx.close()
 
