@@ -8,6 +8,7 @@
 #include <algorithm>
 #include <cstring>
 #include <string>
+#include <type_traits>
 #include <vector>
 
 #include "launch.h"
@@ -101,7 +102,7 @@ int check_config(const moe_verify_config* c) {
 int check_step(const moe_verify_config* c, int32_t B, int32_t K, int has_in, int has_argmax, int has_hout) {
   if (B < 1) return fail(MOE_EINVAL, "B = %d, need B >= 1", B);
   if (K < 0) return fail(MOE_EINVAL, "K = %d, need K >= 0", K);
-  const int64_t T = (int64_t)B * (K + 1);
+  const int64_t T = (int64_t)B * ((int64_t)K + 1);
   if (T > c->max_positions) return fail(MOE_EINVAL, "B*(K+1) = %lld exceeds max_positions %d", (long long)T, c->max_positions);
   if (!has_in) return fail(MOE_EINVAL, "hidden_in is NULL");
   if (c->vocab > 0 && !has_argmax) return fail(MOE_EINVAL, "argmax_out is required when vocab > 0");
@@ -127,6 +128,55 @@ struct DeviceGuard {
   }
 };
 
+// Per-pass buffers of the verify step for up to P positions (device memory).
+struct Workspace {
+  int P = 0;                     // capacity in positions
+  float* x_ws = nullptr;         // [P][H] residual stream
+  void* a = nullptr;             // [P][H] normalised rows, in the weight type
+  int32_t* topk_id = nullptr;    // [P][k]
+  float* topk_w = nullptr;       // [P][k]
+  int32_t* row_tok = nullptr;    // [P*k] token of each routed row
+  int32_t* slot_row = nullptr;   // [P*k] routed row of each slot (inverse of the expert-major order)
+  int32_t* row_dst = nullptr;    // [P*k] position-major ybuf row of each routed row (streaming path)
+  int4* work = nullptr;          // GEMM work list
+  int32_t* n_work = nullptr;     // its length
+  int32_t* chunk_cnt = nullptr;  // [chunks][64] expert counts per slot chunk (large-pass plan)
+  void* h = nullptr;             // [P*(k+S)+1][I] SwiGLU rows (+ a sink row for padding stores)
+  void* ybuf = nullptr;          // [P*(k+S)+1][H] expert outputs, one row per slot, weight type
+  mv::Top2* part = nullptr;      // [P][n_pg] LM-head partial records (vocab > 0)
+  int32_t* counts = nullptr;     // [L][E] routed-slot count per expert of the last pass
+};
+
+// Places a workspace for P positions at base, each piece on a 256-byte boundary, and returns
+// its size in bytes; with base == nullptr only the size is computed.
+size_t layout_workspace(const moe_verify_config& g, int n_pg_lm, int P, char* base, Workspace* w) {
+  const size_t es = elem_bytes(g.wdtype), Pz = (size_t)P;
+  const size_t k = g.top_k, KS = g.top_k + g.n_shared, H = g.hidden, I = g.inter;
+  size_t off = 0;
+  auto take = [&](auto** ptr, size_t bytes) {
+    if (base) *ptr = reinterpret_cast<std::remove_pointer_t<std::remove_reference_t<decltype(ptr)>>>(base + off);
+    off += (bytes + 255) / 256 * 256;
+  };
+  Workspace tmp;
+  Workspace& o = w ? *w : tmp;
+  o.P = P;
+  take(&o.x_ws, Pz * H * sizeof(float));
+  take(&o.a, Pz * H * es);
+  take(&o.topk_id, Pz * k * sizeof(int32_t));
+  take(&o.topk_w, Pz * k * sizeof(float));
+  take(&o.row_tok, Pz * k * sizeof(int32_t));
+  take(&o.slot_row, Pz * k * sizeof(int32_t));
+  take(&o.row_dst, Pz * k * sizeof(int32_t));
+  take(&o.work, (size_t)max_work_items(g, P) * sizeof(int4));
+  take(&o.n_work, sizeof(int32_t));
+  take(&o.chunk_cnt, (size_t)mv::plan_chunks(P, g.top_k) * 64 * sizeof(int32_t));
+  take(&o.h, (Pz * KS + 1) * I * es);
+  take(&o.ybuf, (Pz * KS + 1) * H * es);
+  if (g.vocab > 0) take(&o.part, Pz * n_pg_lm * sizeof(mv::Top2));
+  take(&o.counts, (size_t)g.n_layers * g.n_routed * sizeof(int32_t));
+  return off;
+}
+
 }  // namespace
 
 struct moe_verify_ctx {
@@ -142,21 +192,7 @@ struct moe_verify_ctx {
   uint4* up_p = nullptr;
   uint4* down_p = nullptr;
   uint4* lm_p = nullptr;
-  // workspace
-  float* x_ws = nullptr;
-  void* a = nullptr;
-  int32_t* topk_id = nullptr;
-  float* topk_w = nullptr;
-  int32_t* row_tok = nullptr;
-  int32_t* slot_row = nullptr;  // routed row of each slot (inverse of the expert-major order)
-  int32_t* row_dst = nullptr;   // position-major ybuf row of each routed row (streaming GEMM path)
-  int4* work = nullptr;
-  int32_t* n_work = nullptr;
-  int32_t* chunk_cnt = nullptr;  // [chunks][64] expert counts per slot chunk (large-pass plan)
-  void* h = nullptr;
-  void* ybuf = nullptr;  // expert outputs, one row per slot, in the weight element type
-  mv::Top2* part = nullptr;
-  int32_t* counts = nullptr;  // [L][E] routed-slot count per expert, last step
+  Workspace ws;  // the context's per-pass buffers, for max_positions positions
   int last_T = 0, last_layer = 0;  // positions and block of the last MoE block run (debug_plan)
   // draft block (moe_draft_init): packed weights and its own buffers; the projection and
   // block outputs use ybuf, the normalised rows a, the LM partials part, the GEMM work list
@@ -229,31 +265,29 @@ namespace {
 // Launch the MoE block `l` over Tn positions whose residual input is x_in (plus the
 // previous block's ybuf when given; that sum is stored to x_out when given, which may be
 // x_in itself). Leaves the block's per-slot outputs in ybuf.
-int run_block(moe_verify_ctx* c, int l, const float* x_in, const void* ybuf_prev, float* x_out, int Tn,
+int run_block(moe_verify_ctx* c, const Workspace& w, int l, const float* x_in, const void* ybuf_prev, float* x_out, int Tn,
               hipStream_t st) {
   const moe_verify_config& g = c->cfg;
   const int E = g.n_routed, S = g.n_shared, k = g.top_k, KS = k + S, H = g.hidden, I = g.inter;
   const bool tiled = use_tiled(g, Tn);
   const int mb = tiled ? mv::kTileM : mv::kGemmMB;
-  c->last_T = Tn;
-  c->last_layer = l;
   const int wmax = (int)max_work_items(g, Tn, mb);
   mv::PlanArgs pa{};
-  pa.topk_id = c->topk_id;
-  pa.topk_w = c->topk_w;
+  pa.topk_id = w.topk_id;
+  pa.topk_w = w.topk_w;
   pa.Tn = Tn; pa.k = k; pa.E = E; pa.S = S;
-  pa.row_tok = c->row_tok;
-  pa.slot_row = c->slot_row;
-  pa.row_dst = c->row_dst;
-  pa.work = c->work;
-  pa.n_work = c->n_work;
-  pa.counts = c->counts + (size_t)l * E;
+  pa.row_tok = w.row_tok;
+  pa.slot_row = w.slot_row;
+  pa.row_dst = w.row_dst;
+  pa.work = w.work;
+  pa.n_work = w.n_work;
+  pa.counts = w.counts + (size_t)l * E;
   pa.mb = mb;
-  pa.chunk_cnt = c->chunk_cnt;
+  pa.chunk_cnt = w.chunk_cnt;
   c->prof_begin(MOE_PROF_NORM_ROUTE, st);
-  MV_CHECK(mv::launch_norm_route(g.wdtype, true, x_in, ybuf_prev, c->slot_row, x_out, nullptr, c->a,
-                                 c->router_p + l * c->router_units_per_layer, c->bias_p + (size_t)l * 64, c->topk_id,
-                                 c->topk_w, Tn, H, S, E, k, g.rms_eps, tiled, !tiled, st));
+  MV_CHECK(mv::launch_norm_route(g.wdtype, true, x_in, ybuf_prev, w.slot_row, x_out, nullptr, w.a,
+                                 c->router_p + l * c->router_units_per_layer, c->bias_p + (size_t)l * 64, w.topk_id,
+                                 w.topk_w, Tn, H, S, E, k, g.rms_eps, tiled, !tiled, st));
   c->prof_end(st);
   // small streaming passes: the gate/up GEMM builds the plan in its prologue
   const bool self_plan = !tiled && Tn * k <= mv::kSelfPlanMaxSlots;
@@ -263,19 +297,19 @@ int run_block(moe_verify_ctx* c, int l, const float* x_in, const void* ybuf_prev
     c->prof_end(st);
   }
   mv::GemmArgs a{};
-  a.work = c->work;
-  a.n_work = c->n_work;
+  a.work = w.work;
+  a.n_work = w.n_work;
   a.Tn = Tn;
   a.k = k; a.E = E; a.KS = KS; a.H = H; a.I = I;
-  a.row_tok = c->row_tok;
-  a.row_dst = c->row_dst;
+  a.row_tok = w.row_tok;
+  a.row_dst = w.row_dst;
   a.max_items = wmax;
-  a.sink_row = g.max_positions * KS;  // the extra row past every real row of h and ybuf
-  a.topk_id = c->topk_id;
-  a.plan_work = c->work;
-  a.plan_n_work = c->n_work;
+  a.sink_row = w.P * KS;  // the extra row past every real row of h and ybuf
+  a.topk_id = w.topk_id;
+  a.plan_work = w.work;
+  a.plan_n_work = w.n_work;
   a.plan_counts = pa.counts;
-  a.plan_row_dst = c->row_dst;
+  a.plan_row_dst = w.row_dst;
   a.mb = mb;
   // Streaming kernel: two pairs per wavefront when the expected items x pairs fill at
   // least one round of resident wavefronts (routed items: one per touched expert while
@@ -292,22 +326,22 @@ int run_block(moe_verify_ctx* c, int l, const float* x_in, const void* ybuf_prev
     return tiled ? mv::launch_gemm_tiled(epi, a, n_wg, st) : mv::launch_gemm(g.wdtype, epi, a, n_wg, st);
   };
   // gate/up + SwiGLU
-  a.A = c->a;
+  a.A = w.a;
   a.B = c->up_p + l * c->up_units_per_layer;
   a.K = H;
   a.NQ = c->NQ_up;
-  a.h = c->h;
+  a.h = w.h;
   c->prof_begin(MOE_PROF_GEMM_UP, st);
   unsigned n_wg = grid_for(c->NQ_up, mv::kStreamWavesUp, &a.ppw);
   if (self_plan) MV_CHECK(mv::launch_gemm_planned(g.wdtype, a, n_wg, st));
   else MV_CHECK(launch(mv::EPI_UP, n_wg));
   c->prof_end(st);
   // down + gate scale
-  a.A = c->h;
+  a.A = w.h;
   a.B = c->down_p + l * c->down_units_per_layer;
   a.K = I;
   a.NQ = c->NQ_dn;
-  a.ybuf = c->ybuf;
+  a.ybuf = w.ybuf;
   c->prof_begin(MOE_PROF_GEMM_DOWN, st);
   n_wg = grid_for(c->NQ_dn, mv::kStreamWavesDown, &a.ppw);
   MV_CHECK(launch(mv::EPI_DOWN, n_wg));
@@ -358,7 +392,7 @@ MV_API int moe_verify_init(const moe_verify_config* cfg, const moe_verify_weight
     return fail(MOE_EDEVICE, "device query: %s", hipGetErrorString(he));
   }
   if (c->n_cu < 1) c->n_cu = 1;
-  const int E = g.n_routed, S = g.n_shared, k = g.top_k, KS = k + S, H = g.hidden, I = g.inter, L = g.n_layers;
+  const int E = g.n_routed, S = g.n_shared, H = g.hidden, I = g.inter, L = g.n_layers;
   const size_t es = c->es, P = (size_t)g.max_positions;
   c->NKB_H = (int)(H * es / mv::kRowBlockBytes);
   c->NKB_I = (int)(I * es / mv::kRowBlockBytes);
@@ -370,7 +404,6 @@ MV_API int moe_verify_init(const moe_verify_config* cfg, const moe_verify_weight
   c->up_units_per_layer = (size_t)(E + S) * c->NQ_up * c->NKB_H * mv::kPairUnits;
   c->down_units_per_layer = (size_t)(E + S) * c->NQ_dn * c->NKB_I * mv::kPairUnits;
   const size_t lm_units = (size_t)c->NQ_lm * c->NKB_H * mv::kPairUnits;
-  const size_t wmax = (size_t)max_work_items(g, g.max_positions);
 
   hipError_t ae = hipSuccess;
   auto A = [&](auto** p, size_t bytes) {
@@ -381,21 +414,10 @@ MV_API int moe_verify_init(const moe_verify_config* cfg, const moe_verify_weight
   A(&c->up_p, c->up_units_per_layer * L * 16);
   A(&c->down_p, c->down_units_per_layer * L * 16);
   if (g.vocab > 0) A(&c->lm_p, lm_units * 16);
-  A(&c->x_ws, P * H * sizeof(float));
-  A(&c->a, P * H * es);
-  A(&c->topk_id, P * k * sizeof(int32_t));
-  A(&c->topk_w, P * k * sizeof(float));
-  A(&c->row_tok, P * k * sizeof(int32_t));
-  A(&c->slot_row, P * k * sizeof(int32_t));
-  A(&c->row_dst, P * k * sizeof(int32_t));
-  A(&c->work, wmax * sizeof(int4));
-  A(&c->n_work, sizeof(int32_t));
-  A(&c->chunk_cnt, (size_t)mv::plan_chunks(g.max_positions, k) * 64 * sizeof(int32_t));
-  // h and ybuf rows: every slot's row plus one sink row for the tiled GEMM's padding stores
-  A(&c->h, (P * KS + 1) * I * es);
-  A(&c->ybuf, (P * KS + 1) * H * es);
-  if (g.vocab > 0) A(&c->part, P * c->n_pg_lm * sizeof(mv::Top2));
-  A(&c->counts, (size_t)L * E * sizeof(int32_t));
+  // the per-pass workspace: one allocation laid out by layout_workspace
+  char* ws_base = nullptr;
+  A(&ws_base, layout_workspace(g, c->n_pg_lm, (int)P, nullptr, nullptr));
+  if (ae == hipSuccess) layout_workspace(g, c->n_pg_lm, (int)P, ws_base, &c->ws);
   if (ae != hipSuccess) {
     delete c;
     (void)hipGetLastError();
@@ -411,7 +433,7 @@ MV_API int moe_verify_init(const moe_verify_config* cfg, const moe_verify_weight
     return bail(he, "router repack");
   if ((he = hipMemsetAsync(c->bias_p, 0, (size_t)L * 64 * sizeof(float), st)) != hipSuccess) return bail(he, "bias clear");
   // a work list that no plan has written yet holds no items
-  if ((he = hipMemsetAsync(c->n_work, 0, sizeof(int32_t), st)) != hipSuccess) return bail(he, "work count clear");
+  if ((he = hipMemsetAsync(c->ws.n_work, 0, sizeof(int32_t), st)) != hipSuccess) return bail(he, "work count clear");
   if (w->router_bias &&
       (he = hipMemcpy2DAsync(c->bias_p, 64 * sizeof(float), w->router_bias, E * sizeof(float), E * sizeof(float), L,
                              hipMemcpyDeviceToDevice, st)) != hipSuccess)
@@ -434,8 +456,8 @@ MV_API int moe_verify_init(const moe_verify_config* cfg, const moe_verify_weight
 
 namespace {
 
-// LM head and argmax over the normalised rows row0 .. row0 + Tn - 1 of c->a.
-int run_lm_head(moe_verify_ctx* c, int row0, int Tn, int32_t* argmax_out, float* margin_out, hipStream_t st) {
+// LM head and argmax over the normalised rows row0 .. row0 + Tn - 1 of w.a.
+int run_lm_head(moe_verify_ctx* c, const Workspace& w, int row0, int Tn, int32_t* argmax_out, float* margin_out, hipStream_t st) {
   const moe_verify_config& g = c->cfg;
   // Workgroups (kLmWaves wavefronts, one per CU) cover one row block of up to kLmRows
   // positions; pairs per wavefront so that the workgroups of one row block make about
@@ -445,20 +467,20 @@ int run_lm_head(moe_verify_ctx* c, int row0, int Tn, int32_t* argmax_out, float*
   const int ppw = std::max(1, (c->NQ_lm + target - 1) / target);
   const int n_pg = (c->NQ_lm + mv::kLmWaves * ppw - 1) / (mv::kLmWaves * ppw);
   mv::GemmArgs a{};
-  a.A = static_cast<const char*>(c->a) + (size_t)row0 * g.hidden * c->es;
+  a.A = static_cast<const char*>(w.a) + (size_t)row0 * g.hidden * c->es;
   a.B = c->lm_p;
   a.K = g.hidden;
   a.NQ = c->NQ_lm;
   a.n_valid = g.vocab;
   a.Tn = Tn;
-  a.part = c->part;
+  a.part = w.part;
   a.n_pg = n_pg;
   a.lm_ppw = ppw;
   c->prof_begin(MOE_PROF_LM_HEAD, st);
   MV_CHECK(mv::launch_gemm(g.wdtype, mv::EPI_LM, a, (unsigned)(n_items * n_pg), st));
   c->prof_end(st);
   c->prof_begin(MOE_PROF_ARGMAX, st);
-  MV_CHECK(mv::launch_argmax_reduce(c->part, n_pg, Tn, argmax_out, margin_out, st));
+  MV_CHECK(mv::launch_argmax_reduce(w.part, n_pg, Tn, argmax_out, margin_out, st));
   c->prof_end(st);
   return MOE_OK;
 }
@@ -469,7 +491,7 @@ namespace {
 
 // The MoE blocks over Tn = n_prefill + Tv positions, the final norm, and the LM head and
 // argmax over the last Tv of them.
-int run_pass(moe_verify_ctx* c, const float* hidden_in, int n_prefill, int Tv, int32_t* argmax_out, float* margin_out,
+int run_pass(moe_verify_ctx* c, const Workspace& w, const float* hidden_in, int n_prefill, int Tv, int32_t* argmax_out, float* margin_out,
              float* hidden_out, hipStream_t st) {
   const moe_verify_config& g = c->cfg;
   const int Tn = n_prefill + Tv;
@@ -479,17 +501,16 @@ int run_pass(moe_verify_ctx* c, const float* hidden_in, int n_prefill, int Tv, i
   c->n_pairs = 0;
   for (int l = 0; l < g.n_layers; ++l) {
     // block 0's residual is hidden_in itself: block 1 reads it there, so it is not copied
-    rc = run_block(c, l, l <= 1 ? hidden_in : c->x_ws, l == 0 ? nullptr : c->ybuf, l == 0 ? nullptr : c->x_ws, Tn, st);
+    rc = run_block(c, w, l, l <= 1 ? hidden_in : w.x_ws, l == 0 ? nullptr : w.ybuf, l == 0 ? nullptr : w.x_ws, Tn, st);
     if (rc) return rc;
   }
-  const int KS = g.top_k + g.n_shared;
   c->prof_begin(MOE_PROF_NORM_ROUTE, st);
-  MV_CHECK(mv::launch_norm_route(g.wdtype, false, g.n_layers == 1 ? hidden_in : c->x_ws, c->ybuf, c->slot_row, nullptr, hidden_out,
-                                 g.vocab > 0 ? c->a : nullptr, nullptr, nullptr, nullptr, c->topk_w, Tn, g.hidden,
+  MV_CHECK(mv::launch_norm_route(g.wdtype, false, g.n_layers == 1 ? hidden_in : w.x_ws, w.ybuf, w.slot_row, nullptr, hidden_out,
+                                 g.vocab > 0 ? w.a : nullptr, nullptr, nullptr, nullptr, w.topk_w, Tn, g.hidden,
                                  g.n_shared, g.n_routed, g.top_k, g.rms_eps, false, !use_tiled(g, Tn), st));
   c->prof_end(st);
   if (g.vocab > 0) {
-    rc = run_lm_head(c, n_prefill, Tv, argmax_out, margin_out, st);
+    rc = run_lm_head(c, w, n_prefill, Tv, argmax_out, margin_out, st);
     if (rc) return rc;
   }
   return MOE_OK;
@@ -502,9 +523,12 @@ MV_API int moe_verify_step(moe_verify_ctx* c, const float* hidden_in, int32_t B,
   if (!c) return fail(MOE_EINVAL, "context is NULL");
   const int rc = check_step(&c->cfg, B, K, hidden_in != nullptr, argmax_out != nullptr, hidden_out != nullptr);
   if (rc) return rc;
-  const int rp = run_pass(c, hidden_in, 0, B * (K + 1), argmax_out, margin_out, hidden_out,
+  const int rp = run_pass(c, c->ws, hidden_in, 0, B * (K + 1), argmax_out, margin_out, hidden_out,
                           static_cast<hipStream_t>(stream));
-  return rp ? rp : ok();
+  if (rp) return rp;
+  c->last_T = B * (K + 1);
+  c->last_layer = c->cfg.n_layers - 1;
+  return ok();
 }
 
 MV_API int moe_verify_step_mixed(moe_verify_ctx* c, const float* hidden_in, int32_t n_prefill, int32_t B, int32_t K,
@@ -514,12 +538,15 @@ MV_API int moe_verify_step_mixed(moe_verify_ctx* c, const float* hidden_in, int3
   const moe_verify_config& g = c->cfg;
   int rc = check_step(&g, B, K, hidden_in != nullptr, argmax_out != nullptr, hidden_out != nullptr);
   if (rc) return rc;
-  if ((int64_t)n_prefill + (int64_t)B * (K + 1) > g.max_positions)
+  if ((int64_t)n_prefill + (int64_t)B * ((int64_t)K + 1) > g.max_positions)
     return fail(MOE_EINVAL, "n_prefill + B*(K+1) = %lld exceeds max_positions %d",
-                (long long)n_prefill + (long long)B * (K + 1), g.max_positions);
-  rc = run_pass(c, hidden_in, n_prefill, B * (K + 1), argmax_out, margin_out, hidden_out,
+                (long long)n_prefill + (long long)B * ((long long)K + 1), g.max_positions);
+  rc = run_pass(c, c->ws, hidden_in, n_prefill, B * (K + 1), argmax_out, margin_out, hidden_out,
                 static_cast<hipStream_t>(stream));
-  return rc ? rc : ok();
+  if (rc) return rc;
+  c->last_T = n_prefill + B * (K + 1);
+  c->last_layer = g.n_layers - 1;
+  return ok();
 }
 
 MV_API int accept_greedy(const int32_t* draft_ids, const int32_t* argmax_ids, int32_t B, int32_t K,
@@ -542,15 +569,16 @@ MV_API int moe_verify_debug_layer(moe_verify_ctx* c, int32_t layer, const float*
   hipStream_t st = static_cast<hipStream_t>(stream);
   DeviceGuard dg(c->device);
   if (dg.err != hipSuccess) return fail(MOE_EDEVICE, "device select: %s", hipGetErrorString(dg.err));
-  int rc = run_block(c, layer, x_in, nullptr, nullptr, T, st);
+  int rc = run_block(c, c->ws, layer, x_in, nullptr, nullptr, T, st);
   if (rc) return rc;
-  const int KS = g.top_k + g.n_shared;
+  c->last_T = T;
+  c->last_layer = layer;
   if (moe_out)
-    MV_CHECK(mv::launch_combine(g.wdtype, c->ybuf, c->slot_row, c->topk_w, T, g.hidden, g.top_k, g.n_shared, !use_tiled(g, T),
+    MV_CHECK(mv::launch_combine(g.wdtype, c->ws.ybuf, c->ws.slot_row, c->ws.topk_w, T, g.hidden, g.top_k, g.n_shared, !use_tiled(g, T),
                                 moe_out, st));
   const size_t kb = (size_t)T * g.top_k * 4;
-  if (topk_id) MV_CHECK(hipMemcpyAsync(topk_id, c->topk_id, kb, hipMemcpyDeviceToDevice, st));
-  if (topk_w) MV_CHECK(hipMemcpyAsync(topk_w, c->topk_w, kb, hipMemcpyDeviceToDevice, st));
+  if (topk_id) MV_CHECK(hipMemcpyAsync(topk_id, c->ws.topk_id, kb, hipMemcpyDeviceToDevice, st));
+  if (topk_w) MV_CHECK(hipMemcpyAsync(topk_w, c->ws.topk_w, kb, hipMemcpyDeviceToDevice, st));
   return ok();
 }
 
@@ -566,11 +594,11 @@ MV_API int moe_verify_debug_head(moe_verify_ctx* c, const float* x_in, int32_t T
   if (dg.err != hipSuccess) return fail(MOE_EDEVICE, "device select: %s", hipGetErrorString(dg.err));
   // the final norm with no expert outputs to add: a = RMSNorm(x_in) in the weight type
   c->prof_begin(MOE_PROF_NORM_ROUTE, st);
-  MV_CHECK(mv::launch_norm_route(g.wdtype, false, x_in, nullptr, nullptr, nullptr, nullptr, c->a, nullptr, nullptr,
+  MV_CHECK(mv::launch_norm_route(g.wdtype, false, x_in, nullptr, nullptr, nullptr, nullptr, c->ws.a, nullptr, nullptr,
                                  nullptr, nullptr, T, g.hidden, g.n_shared, g.n_routed, g.top_k, g.rms_eps, false,
                                  true, st));
   c->prof_end(st);
-  const int rc = run_lm_head(c, 0, T, argmax_out, margin_out, st);
+  const int rc = run_lm_head(c, c->ws, 0, T, argmax_out, margin_out, st);
   return rc ? rc : ok();
 }
 
@@ -582,9 +610,9 @@ MV_API int moe_verify_debug_plan(moe_verify_ctx* c, int32_t* row_slot, int32_t* 
   hipStream_t st = static_cast<hipStream_t>(stream);
   DeviceGuard dg(c->device);
   if (dg.err != hipSuccess) return fail(MOE_EDEVICE, "device select: %s", hipGetErrorString(dg.err));
-  MV_CHECK(mv::launch_row_slot(c->row_dst, c->last_T * g.top_k, g.top_k, g.top_k + g.n_shared, row_slot, st));
+  MV_CHECK(mv::launch_row_slot(c->ws.row_dst, c->last_T * g.top_k, g.top_k, g.top_k + g.n_shared, row_slot, st));
   if (counts)
-    MV_CHECK(hipMemcpyAsync(counts, c->counts + (size_t)c->last_layer * g.n_routed, (size_t)g.n_routed * sizeof(int32_t),
+    MV_CHECK(hipMemcpyAsync(counts, c->ws.counts + (size_t)c->last_layer * g.n_routed, (size_t)g.n_routed * sizeof(int32_t),
                             hipMemcpyDeviceToDevice, st));
   return ok();
 }
@@ -657,8 +685,8 @@ MV_API int moe_draft_step(moe_verify_ctx* c, const float* hidden, const int32_t*
   if (B < 1) return fail(MOE_EINVAL, "B = %d, need B >= 1", B);
   if (Kv < 0) return fail(MOE_EINVAL, "Kv = %d, need Kv >= 0", Kv);
   if (K < 1) return fail(MOE_EINVAL, "K = %d, need K >= 1", K);
-  if ((int64_t)B * (Kv + 1) > g.max_positions)
-    return fail(MOE_EINVAL, "B*(Kv+1) = %lld exceeds max_positions %d", (long long)B * (Kv + 1), g.max_positions);
+  if ((int64_t)B * ((int64_t)Kv + 1) > g.max_positions)
+    return fail(MOE_EINVAL, "B*(Kv+1) = %lld exceeds max_positions %d", (long long)B * ((long long)Kv + 1), g.max_positions);
   if (!hidden || !accepted_len || !committed || !drafts) return fail(MOE_EINVAL, "a required pointer is NULL");
   hipStream_t st = static_cast<hipStream_t>(stream);
   DeviceGuard dg(c->device);
@@ -667,8 +695,8 @@ MV_API int moe_draft_step(moe_verify_ctx* c, const float* hidden, const int32_t*
   const int max_items = (g.max_positions + mb - 1) / mb;
   // The GEMMs see one always-on expert (routed count 0) whose work items are row blocks.
   mv::GemmArgs a{};
-  a.work = c->work;
-  a.n_work = c->n_work;
+  a.work = c->ws.work;
+  a.n_work = c->ws.n_work;
   a.Tn = B;
   a.k = 0; a.E = 0; a.KS = 1; a.H = H; a.I = Id;
   a.max_items = max_items;
@@ -678,30 +706,30 @@ MV_API int moe_draft_step(moe_verify_ctx* c, const float* hidden, const int32_t*
     *ppw = items * NQ >= wave_target ? 2 : 1;
     return (unsigned)((max_items * ((NQ + *ppw - 1) / *ppw) + wpg - 1) / wpg);
   };
-  MV_CHECK(mv::launch_draft_plan(c->work, c->n_work, B, mb, st));
+  MV_CHECK(mv::launch_draft_plan(c->ws.work, c->ws.n_work, B, mb, st));
   for (int i = 0; i < K; ++i) {
     MV_CHECK(mv::launch_draft_input(g.wdtype, hidden, accepted_len, committed, Kv, c->draft_z, c->draft_ids, drafts, K,
                                     i, c->lm_p, c->NKB_H, H, g.vocab, g.rms_eps, c->draft_u, B, st));
     // projection 2H -> H (an output-side GEMM like the experts' down projection)
     mv::GemmArgs p = a;
-    p.A = c->draft_u; p.B = c->draft_proj_p; p.K = 2 * H; p.NQ = (H + 31) / 32; p.ybuf = c->ybuf;
+    p.A = c->draft_u; p.B = c->draft_proj_p; p.K = 2 * H; p.NQ = (H + 31) / 32; p.ybuf = c->ws.ybuf;
     unsigned n_wg = grid(p.NQ, mv::kStreamWavesDown, &p.ppw);
     MV_CHECK(mv::launch_gemm(g.wdtype, mv::EPI_DOWN, p, n_wg, st));
     // residual stream z = projection output; a = bf16(RMSNorm(z)) (one unit-gate slot per row)
-    MV_CHECK(mv::launch_norm_route(g.wdtype, false, c->draft_zero, c->ybuf, nullptr, c->draft_z, nullptr, c->a, nullptr,
+    MV_CHECK(mv::launch_norm_route(g.wdtype, false, c->draft_zero, c->ws.ybuf, nullptr, c->draft_z, nullptr, c->ws.a, nullptr,
                                    nullptr, nullptr, c->draft_ones, B, H, 0, 0, 1, g.rms_eps, false, true, st));
     mv::GemmArgs u = a;  // gate/up + SwiGLU
-    u.A = c->a; u.B = c->draft_up_p; u.K = H; u.NQ = Id / 16; u.h = c->draft_h;
+    u.A = c->ws.a; u.B = c->draft_up_p; u.K = H; u.NQ = Id / 16; u.h = c->draft_h;
     n_wg = grid(u.NQ, mv::kStreamWavesUp, &u.ppw);
     MV_CHECK(mv::launch_gemm(g.wdtype, mv::EPI_UP, u, n_wg, st));
     mv::GemmArgs d = a;  // down
-    d.A = c->draft_h; d.B = c->draft_down_p; d.K = Id; d.NQ = (H + 31) / 32; d.ybuf = c->ybuf;
+    d.A = c->draft_h; d.B = c->draft_down_p; d.K = Id; d.NQ = (H + 31) / 32; d.ybuf = c->ws.ybuf;
     n_wg = grid(d.NQ, mv::kStreamWavesDown, &d.ppw);
     MV_CHECK(mv::launch_gemm(g.wdtype, mv::EPI_DOWN, d, n_wg, st));
     // z <- z + block output; a = bf16(RMSNorm(z)) for the LM head
-    MV_CHECK(mv::launch_norm_route(g.wdtype, false, c->draft_z, c->ybuf, nullptr, c->draft_z, nullptr, c->a, nullptr,
+    MV_CHECK(mv::launch_norm_route(g.wdtype, false, c->draft_z, c->ws.ybuf, nullptr, c->draft_z, nullptr, c->ws.a, nullptr,
                                    nullptr, nullptr, c->draft_ones, B, H, 0, 0, 1, g.rms_eps, false, true, st));
-    const int rc = run_lm_head(c, 0, B, c->draft_ids, nullptr, st);
+    const int rc = run_lm_head(c, c->ws, 0, B, c->draft_ids, nullptr, st);
     if (rc) return rc;
   }
   MV_CHECK(mv::launch_draft_store(c->draft_ids, drafts, B, K, st));
@@ -760,7 +788,7 @@ MV_API int moe_verify_expert_counts(moe_verify_ctx* c, int32_t* counts) {
   DeviceGuard dg(c->device);
   if (dg.err != hipSuccess) return fail(MOE_EDEVICE, "device select: %s", hipGetErrorString(dg.err));
   MV_CHECK(hipDeviceSynchronize());
-  MV_CHECK(hipMemcpy(counts, c->counts, (size_t)c->cfg.n_layers * c->cfg.n_routed * sizeof(int32_t),
+  MV_CHECK(hipMemcpy(counts, c->ws.counts, (size_t)c->cfg.n_layers * c->cfg.n_routed * sizeof(int32_t),
                      hipMemcpyDeviceToHost));
   return ok();
 }
