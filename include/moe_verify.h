@@ -141,6 +141,22 @@ int moe_verify_step_mixed(moe_verify_ctx *ctx, const float *hidden_in, int32_t n
                           int32_t K, int32_t *argmax_out, float *margin_out, float *hidden_out,
                           void *stream);
 
+/* Bytes of the device array behind moe_verify_step_static (one copy per GPU). */
+#define MOE_VERIFY_STATIC_SCRATCH_BYTES (32u << 20)
+
+/* moe_verify_step for callers that cannot allocate device memory at all (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the same pass, same
+ * arguments, same results bit for bit, but every per-pass buffer (residual stream,
+ * normalised rows, routing and plan, SwiGLU rows, expert outputs, LM-head partials) comes
+ * from one file-scope device array of MOE_VERIFY_STATIC_SCRATCH_BYTES per GPU instead of
+ * the context's workspace; the call allocates and frees nothing. MOE_EUNSUPPORTED when the
+ * pass's buffers exceed that size (about 23 MB for 512 positions of the real-width model).
+ * All calls on one GPU share that GPU's array, which keeps the last call's contents: calls
+ * that overlap on one GPU (any context, any stream) race. moe_verify_expert_counts and
+ * moe_verify_debug_plan describe the context's own passes, not these. */
+int moe_verify_step_static(moe_verify_ctx *ctx, const float *hidden_in, int32_t B, int32_t K,
+                           int32_t *argmax_out, float *margin_out, float *hidden_out, void *stream);
+
 /* Greedy acceptance for B sequences of K drafts.
  *   draft_ids    [B][K] int32 device (ids outside [0, V) simply never match);
  *   argmax_ids   [B][K+1] int32 device (the step's argmax_out);

@@ -20,7 +20,8 @@ MOE_F32, MOE_BF16 = 0, 1
 EXPORTS = ("moe_verify_check_config", "moe_verify_check_step", "moe_verify_init", "moe_verify_step",
            "accept_greedy", "moe_verify_destroy", "moe_verify_last_error", "moe_verify_debug_layer",
            "moe_verify_profile", "moe_verify_profile_read", "moe_verify_expert_counts", "moe_draft_init",
-           "moe_draft_step", "moe_verify_step_mixed", "moe_verify_debug_head", "moe_verify_debug_plan")
+           "moe_draft_step", "moe_verify_step_mixed", "moe_verify_debug_head", "moe_verify_debug_plan",
+           "moe_verify_step_static")
 PROF_KINDS = ("norm_route", "plan", "gemm_up", "gemm_down", "lm_head", "argmax")
 
 
@@ -81,6 +82,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     L.moe_draft_step.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, vp]
     L.moe_verify_debug_head.argtypes = [vp, vp, i32, vp, f32p, vp]
     L.moe_verify_debug_plan.argtypes = [vp, vp, vp, vp]
+    L.moe_verify_step_static.argtypes = [vp, vp, i32, i32, vp, f32p, f32p, vp]
     for name in EXPORTS:
         if name not in ("moe_verify_destroy", "moe_verify_last_error"):
             getattr(L, name).restype = ctypes.c_int
@@ -167,6 +169,12 @@ class MoeVerify:
     def step(self, hidden_in, B: int, K: int, argmax_out=None, margin_out=None, hidden_out=None, stream=None):
         _check(load_library().moe_verify_step(self._h, _ptr(hidden_in), B, K, _ptr(argmax_out), _ptr(margin_out),
                                               _ptr(hidden_out), _stream(stream)), "moe_verify_step")
+
+    def step_static(self, hidden_in, B: int, K: int, argmax_out=None, margin_out=None, hidden_out=None,
+                    stream=None):
+        _check(load_library().moe_verify_step_static(self._h, _ptr(hidden_in), B, K, _ptr(argmax_out),
+                                                     _ptr(margin_out), _ptr(hidden_out), _stream(stream)),
+               "moe_verify_step_static")
 
     def step_mixed(self, hidden_in, n_prefill: int, B: int, K: int, argmax_out=None, margin_out=None,
                    hidden_out=None, stream=None):

@@ -7,6 +7,7 @@
 #include <cstdio>
 #include <algorithm>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <type_traits>
 #include <vector>
@@ -254,6 +255,35 @@ struct moe_verify_ctx {
   }
 };
 
+// ---- per-pass buffers without allocation ------------------------------------------------
+// moe_verify_step_static takes every per-pass buffer from this device array (one copy per GPU,
+// held until the process ends). Host code never hands the array's name to a kernel: the
+// device address of each GPU's copy comes from hipGetSymbolAddress, resolved once per device
+// with that device current, and only that address is used.
+static __device__ __align__(256) char scratch[MOE_VERIFY_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's copy of `scratch` (dev must be current).
+hipError_t scratch_address(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
 namespace {
 
 #define MV_CHECK(call)                                                                          \
@@ -450,6 +480,10 @@ MV_API int moe_verify_init(const moe_verify_config* cfg, const moe_verify_weight
                                     (size_t)g.vocab * row_h, st)) != hipSuccess)
     return bail(he, "lm_head repack");
   if ((he = hipStreamSynchronize(st)) != hipSuccess) return bail(he, "repack");
+  // this device's static scratch (moe_verify_step_static): resolved here, while the device is
+  // current; a failure is reported by that call, which retries
+  void* scratch_dev = nullptr;
+  if (scratch_address(c->device, &scratch_dev) != hipSuccess) (void)hipGetLastError();
   *out = c;
   return ok();
 }
@@ -547,6 +581,29 @@ MV_API int moe_verify_step_mixed(moe_verify_ctx* c, const float* hidden_in, int3
   c->last_T = n_prefill + B * (K + 1);
   c->last_layer = g.n_layers - 1;
   return ok();
+}
+
+MV_API int moe_verify_step_static(moe_verify_ctx* c, const float* hidden_in, int32_t B, int32_t K,
+                                  int32_t* argmax_out, float* margin_out, float* hidden_out, void* stream) {
+  if (!c) return fail(MOE_EINVAL, "context is NULL");
+  const moe_verify_config& g = c->cfg;
+  const int rc = check_step(&g, B, K, hidden_in != nullptr, argmax_out != nullptr, hidden_out != nullptr);
+  if (rc) return rc;
+  const int T = B * (K + 1);
+  const size_t need = layout_workspace(g, c->n_pg_lm, T, nullptr, nullptr);
+  if (need > (size_t)MOE_VERIFY_STATIC_SCRATCH_BYTES)
+    return fail(MOE_EUNSUPPORTED, "a pass of %d positions needs %zu bytes of per-pass buffers; the static scratch holds %zu",
+                T, need, (size_t)MOE_VERIFY_STATIC_SCRATCH_BYTES);
+  DeviceGuard dg(c->device);
+  if (dg.err != hipSuccess) return fail(MOE_EDEVICE, "device select: %s", hipGetErrorString(dg.err));
+  void* base = nullptr;
+  const hipError_t e = scratch_address(c->device, &base);
+  if (e != hipSuccess) return fail(MOE_EDEVICE, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+  // every buffer of the pass is written before it is read, so nothing needs clearing
+  Workspace w;
+  layout_workspace(g, c->n_pg_lm, T, static_cast<char*>(base), &w);
+  const int rp = run_pass(c, w, hidden_in, 0, T, argmax_out, margin_out, hidden_out, static_cast<hipStream_t>(stream));
+  return rp ? rp : ok();
 }
 
 MV_API int accept_greedy(const int32_t* draft_ids, const int32_t* argmax_ids, int32_t B, int32_t K,

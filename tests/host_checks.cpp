@@ -83,6 +83,7 @@ int main() {
   const float* hp = reinterpret_cast<const float*>(0x100);
   int32_t* ip = reinterpret_cast<int32_t*>(0x100);
   EXPECT(moe_verify_step(nullptr, hp, 1, 3, ip, nullptr, nullptr, nullptr) == MOE_EINVAL);
+  EXPECT(moe_verify_step_static(nullptr, hp, 1, 3, ip, nullptr, nullptr, nullptr) == MOE_EINVAL);
   EXPECT(moe_verify_step_mixed(nullptr, hp, 4, 1, 3, ip, nullptr, nullptr, nullptr) == MOE_EINVAL);
   EXPECT(moe_verify_debug_layer(nullptr, 0, hp, 4, nullptr, nullptr, nullptr, nullptr) == MOE_EINVAL);
   EXPECT(moe_verify_debug_head(nullptr, hp, 4, ip, nullptr, nullptr) == MOE_EINVAL);

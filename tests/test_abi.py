@@ -142,6 +142,7 @@ def test_entry_points_reject_before_any_device_call(lib):
     assert lib.moe_verify_step_mixed(None, 16, 8, 1, 3, 16, None, None, None) == bnd.MOE_EINVAL
     assert lib.moe_verify_debug_head(None, 16, 4, 16, None, None) == bnd.MOE_EINVAL
     assert lib.moe_verify_debug_plan(None, 16, None, None) == bnd.MOE_EINVAL
+    assert lib.moe_verify_step_static(None, 16, 1, 3, 16, None, None, None) == bnd.MOE_EINVAL
     # acceptance
     assert lib.accept_greedy(16, 16, 0, 3, 16, 16, None) == bnd.MOE_EINVAL
     assert lib.accept_greedy(16, 16, 1, -1, 16, 16, None) == bnd.MOE_EINVAL
