@@ -47,8 +47,8 @@ constexpr int kTileStages = 4;
 constexpr int kRunUnits = kWave;       // 16-byte units per 1 KB run
 constexpr int kStageRuns = 16;         // runs per operand per stage
 constexpr int kLoadsPerStage = 4;      // direct loads per wavefront per stage
-constexpr int kUpStores = 16;          // epilogue stores per wavefront: UP 8 rows x 2 pairs
-constexpr int kDownStores = 32;        //   DOWN 8 rows x 2 pairs x 2 tiles
+constexpr int kUpStores = 8;           // epilogue stores per wavefront: UP 8 row tiles
+constexpr int kDownStores = 16;        //   DOWN 8 row tiles x 2 pairs
 
 // s_waitcnt for at most N vector-memory operations of this wavefront still in flight and
 // none of its LDS operations (expcnt left unconstrained).
@@ -70,6 +70,12 @@ __device__ __forceinline__ void lds_load16(const void* gptr, const void* lds) {
 __device__ __forceinline__ void lds_load4(const void* gptr, const void* lds) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(m0), "v"(gptr) : "memory", "m0");
+}
+// Two float32 values to a packed pair of bf16 (round to nearest even, one instruction).
+typedef float f32x2_cv_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_cv_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_cv_t){a, b}, bf16x2_cv_t));
 }
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
@@ -181,39 +187,53 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_moe_tiled(GemmArgs g) {
                                                                   __builtin_bit_cast(bf16x8_t, a[i]),
                                                                   acc[i][pp][t], 0, 0, 0);
   };
-  // Every lane issues exactly NST stores (rows past the item's end and columns past the
-  // last go to the sink row), so the in-flight counts the waits rely on are exact.
+  // Every lane issues exactly NST 16-byte stores (rows past the item's end and columns past
+  // the last go to the sink row), so the in-flight counts the waits rely on are exact. Lane
+  // group gq = l / 16 of a 16x16 result holds columns 4*gq..+3 of position l % 16; one
+  // permlane16 swap between two such results (gate/up: the wavefront's two pairs; down: the
+  // two 16-column tiles of a pair) leaves each lane 8 consecutive columns, so a store
+  // instruction writes 16 positions x 64 contiguous bytes instead of 16 x 32 bytes twice.
   auto epilogue = [&](const TileInfo& t) __attribute__((always_inline)) {
-    const int c4 = 4 * (lane >> 4);  // first of the lane's four output columns in a 16-column tile
+    const int gq = lane >> 4;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int r = 128 * wm + 16 * i + (lane & 15);
       const bool row_ok = r < t.M;
       if constexpr (EPI == EPI_UP) {
+        uint32_t lo[2], hi[2];  // bf16 pairs of columns 4*gq, 4*gq+1 and 4*gq+2, 4*gq+3 of pair pp
 #pragma unroll
         for (int pp = 0; pp < 2; ++pp) {
-          const int q = t.nt * kTilePairs + 2 * wn + pp;
-          uint32_t v[4];
+          float sv[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) v[j] = f32_to_bf16(swiglu(acc[i][pp][0][j], acc[i][pp][1][j]));
-          const size_t off = row_ok && q < g.NQ ? (size_t)(t.row0 + r) * g.I + stage_ordered_elem(q * 16 + c4)
-                                                : (size_t)g.sink_row * g.I;
-          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(g.h) + off) =
-              make_uint2(v[0] | (v[1] << 16), v[2] | (v[3] << 16));
+          for (int j = 0; j < 4; ++j) sv[j] = swiglu(acc[i][pp][0][j], acc[i][pp][1][j]);
+          lo[pp] = pack_bf16x2(sv[0], sv[1]);
+          hi[pp] = pack_bf16x2(sv[2], sv[3]);
         }
+        // lane group gq now holds columns 8*(gq/2)..+7 of pair 2*wn + gq%2
+        const auto xl = __builtin_amdgcn_permlane16_swap(lo[0], lo[1], false, false);
+        const auto xh = __builtin_amdgcn_permlane16_swap(hi[0], hi[1], false, false);
+        const int q = t.nt * kTilePairs + 2 * wn + (gq & 1);
+        const int e = q * 16 + 8 * (gq >> 1);
+        const size_t off = row_ok && q < g.NQ ? (size_t)(t.row0 + r) * g.I + stage_ordered_elem(e)
+                                              : (size_t)g.sink_row * g.I;
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(g.h) + off) =
+            make_uint4((uint32_t)xl[0], (uint32_t)xh[0], (uint32_t)xl[1], (uint32_t)xh[1]);
       } else {
 #pragma unroll
         for (int pp = 0; pp < 2; ++pp) {
           const int q = t.nt * kTilePairs + 2 * wn + pp;
-#pragma unroll
-          for (int tt = 0; tt < 2; ++tt) {
-            const int col = (2 * q + tt) * 16 + c4;
-            const size_t off = row_ok && q < g.NQ && col < g.H ? (size_t)(t.row0 + r) * g.H + col
-                                                               : (size_t)g.sink_row * g.H;
-            const uint32_t v0 = f32_to_bf16(acc[i][pp][tt][0]), v1 = f32_to_bf16(acc[i][pp][tt][1]);
-            const uint32_t v2 = f32_to_bf16(acc[i][pp][tt][2]), v3 = f32_to_bf16(acc[i][pp][tt][3]);
-            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(g.ybuf) + off) = make_uint2(v0 | (v1 << 16), v2 | (v3 << 16));
-          }
+          const uint32_t d0 = pack_bf16x2(acc[i][pp][0][0], acc[i][pp][0][1]);
+          const uint32_t d1 = pack_bf16x2(acc[i][pp][0][2], acc[i][pp][0][3]);
+          const uint32_t e0 = pack_bf16x2(acc[i][pp][1][0], acc[i][pp][1][1]);
+          const uint32_t e1 = pack_bf16x2(acc[i][pp][1][2], acc[i][pp][1][3]);
+          // lane group gq now holds columns 8*(gq/2)..+7 of the pair's tile gq%2
+          const auto x0 = __builtin_amdgcn_permlane16_swap(d0, e0, false, false);
+          const auto x1 = __builtin_amdgcn_permlane16_swap(d1, e1, false, false);
+          const int col = (2 * q + (gq & 1)) * 16 + 8 * (gq >> 1);
+          const size_t off = row_ok && q < g.NQ && col < g.H ? (size_t)(t.row0 + r) * g.H + col
+                                                             : (size_t)g.sink_row * g.H;
+          *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(g.ybuf) + off) =
+              make_uint4((uint32_t)x0[0], (uint32_t)x1[0], (uint32_t)x0[1], (uint32_t)x1[1]);
         }
       }
     }
