@@ -60,6 +60,16 @@ int64_t max_work_items(const moe_verify_config& c, int64_t T, int64_t mb = mv::k
 bool use_tiled(const moe_verify_config& c, int Tn) {
   return c.wdtype == MOE_BF16 && Tn >= MV_TILED_MIN_POSITIONS && c.hidden >= 256 && c.inter >= 256;
 }
+// The LM head runs on the tiled GEMM (k_moe_tiled<EPI_LM>, 256-row items) from 256 rows on
+// unless the last item would be at most half full: beyond two 128-row blocks the streaming
+// LM head is bound by LDS reads rather than by the weight stream, while a tiled round costs
+// the same for a half-empty item. Measured (one MI355X, full vocabulary): 256 rows 109 vs
+// 122 us streaming, 384: 181 vs 169, 448: 184 vs 226, 512: 185 vs 222, 640: 266 vs 266,
+// 768: 266 vs 307.
+bool use_tiled_lm(const moe_verify_config& c, int Tv) {
+  const int r = Tv % mv::kTileM;
+  return c.wdtype == MOE_BF16 && c.vocab > 0 && c.hidden >= 256 && Tv >= mv::kTileM && (r == 0 || 2 * r > mv::kTileM);
+}
 
 int check_config(const moe_verify_config* c) {
   if (!c) return fail(MOE_EINVAL, "config is NULL");
@@ -173,7 +183,8 @@ size_t layout_workspace(const moe_verify_config& g, int n_pg_lm, int P, char* ba
   take(&o.chunk_cnt, (size_t)mv::plan_chunks(P, g.top_k) * 64 * sizeof(int32_t));
   take(&o.h, (Pz * KS + 1) * I * es);
   take(&o.ybuf, (Pz * KS + 1) * H * es);
-  if (g.vocab > 0) take(&o.part, Pz * n_pg_lm * sizeof(mv::Top2));
+  // (+1: the tiled LM head's lanes without a row store into the slot past the last)
+  if (g.vocab > 0) take(&o.part, (Pz * n_pg_lm + 1) * sizeof(mv::Top2));
   take(&o.counts, (size_t)g.n_layers * g.n_routed * sizeof(int32_t));
   return off;
 }
@@ -490,9 +501,32 @@ MV_API int moe_verify_init(const moe_verify_config* cfg, const moe_verify_weight
 
 namespace {
 
-// LM head and argmax over the normalised rows row0 .. row0 + Tn - 1 of w.a.
-int run_lm_head(moe_verify_ctx* c, const Workspace& w, int row0, int Tn, int32_t* argmax_out, float* margin_out, hipStream_t st) {
+// LM head and argmax over the normalised rows row0 .. row0 + Tn - 1 of w.a, which are in
+// the stage-ordered layout of the tiled GEMM when tiled (use_tiled_lm), else in row order.
+int run_lm_head(moe_verify_ctx* c, const Workspace& w, int row0, int Tn, int32_t* argmax_out, float* margin_out,
+                bool tiled, hipStream_t st) {
   const moe_verify_config& g = c->cfg;
+  if (tiled) {
+    // 256-row items x 256-column tiles, one record per row and column tile
+    const int NT = mv::tiled_tiles_per_item(c->NQ_lm);
+    const int n_tiles = (Tn + mv::kTileM - 1) / mv::kTileM * NT;
+    mv::GemmArgs a{};
+    a.A = static_cast<const char*>(w.a) + (size_t)row0 * g.hidden * c->es;
+    a.B = c->lm_p;
+    a.K = g.hidden;
+    a.NQ = c->NQ_lm;
+    a.n_valid = g.vocab;
+    a.Tn = Tn;
+    a.part = w.part;
+    a.n_pg = NT;
+    c->prof_begin(MOE_PROF_LM_HEAD, st);
+    MV_CHECK(mv::launch_gemm_tiled(mv::EPI_LM, a, (unsigned)std::min(c->n_cu, n_tiles), st));
+    c->prof_end(st);
+    c->prof_begin(MOE_PROF_ARGMAX, st);
+    MV_CHECK(mv::launch_argmax_reduce(w.part, NT, Tn, argmax_out, margin_out, st));
+    c->prof_end(st);
+    return MOE_OK;
+  }
   // Workgroups (kLmWaves wavefronts, one per CU) cover one row block of up to kLmRows
   // positions; pairs per wavefront so that the workgroups of one row block make about
   // one round on the device (further row blocks share the weight stream through L2).
@@ -538,13 +572,14 @@ int run_pass(moe_verify_ctx* c, const Workspace& w, const float* hidden_in, int 
     rc = run_block(c, w, l, l <= 1 ? hidden_in : w.x_ws, l == 0 ? nullptr : w.ybuf, l == 0 ? nullptr : w.x_ws, Tn, st);
     if (rc) return rc;
   }
+  const bool lm_tiled = use_tiled_lm(g, Tv);
   c->prof_begin(MOE_PROF_NORM_ROUTE, st);
   MV_CHECK(mv::launch_norm_route(g.wdtype, false, g.n_layers == 1 ? hidden_in : w.x_ws, w.ybuf, w.slot_row, nullptr, hidden_out,
                                  g.vocab > 0 ? w.a : nullptr, nullptr, nullptr, nullptr, w.topk_w, Tn, g.hidden,
-                                 g.n_shared, g.n_routed, g.top_k, g.rms_eps, false, !use_tiled(g, Tn), st));
+                                 g.n_shared, g.n_routed, g.top_k, g.rms_eps, lm_tiled, !use_tiled(g, Tn), st));
   c->prof_end(st);
   if (g.vocab > 0) {
-    rc = run_lm_head(c, w, n_prefill, Tv, argmax_out, margin_out, st);
+    rc = run_lm_head(c, w, n_prefill, Tv, argmax_out, margin_out, lm_tiled, st);
     if (rc) return rc;
   }
   return MOE_OK;
@@ -650,12 +685,13 @@ MV_API int moe_verify_debug_head(moe_verify_ctx* c, const float* x_in, int32_t T
   DeviceGuard dg(c->device);
   if (dg.err != hipSuccess) return fail(MOE_EDEVICE, "device select: %s", hipGetErrorString(dg.err));
   // the final norm with no expert outputs to add: a = RMSNorm(x_in) in the weight type
+  const bool lm_tiled = use_tiled_lm(g, T);
   c->prof_begin(MOE_PROF_NORM_ROUTE, st);
   MV_CHECK(mv::launch_norm_route(g.wdtype, false, x_in, nullptr, nullptr, nullptr, nullptr, c->ws.a, nullptr, nullptr,
-                                 nullptr, nullptr, T, g.hidden, g.n_shared, g.n_routed, g.top_k, g.rms_eps, false,
+                                 nullptr, nullptr, T, g.hidden, g.n_shared, g.n_routed, g.top_k, g.rms_eps, lm_tiled,
                                  true, st));
   c->prof_end(st);
-  const int rc = run_lm_head(c, c->ws, 0, T, argmax_out, margin_out, st);
+  const int rc = run_lm_head(c, c->ws, 0, T, argmax_out, margin_out, lm_tiled, st);
   return rc ? rc : ok();
 }
 
@@ -786,7 +822,7 @@ MV_API int moe_draft_step(moe_verify_ctx* c, const float* hidden, const int32_t*
     // z <- z + block output; a = bf16(RMSNorm(z)) for the LM head
     MV_CHECK(mv::launch_norm_route(g.wdtype, false, c->draft_z, c->ws.ybuf, nullptr, c->draft_z, nullptr, c->ws.a, nullptr,
                                    nullptr, nullptr, c->draft_ones, B, H, 0, 0, 1, g.rms_eps, false, true, st));
-    const int rc = run_lm_head(c, c->ws, 0, B, c->draft_ids, nullptr, st);
+    const int rc = run_lm_head(c, c->ws, 0, B, c->draft_ids, nullptr, false, st);
     if (rc) return rc;
   }
   MV_CHECK(mv::launch_draft_store(c->draft_ids, drafts, B, K, st));

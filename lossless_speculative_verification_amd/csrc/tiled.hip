@@ -6,7 +6,11 @@
 //   UP:   h = bf16(silu(A W_gate^T) * (A W_up^T)) for the expert's rows of A
 //   DOWN: y = bf16(h W_down^T), written to the same row of ybuf as the row of h
 // with the same row space, work list, outputs and float32 accumulation as the
-// streaming kernels (k_moe_gemm), so either path can run any block.
+// streaming kernels (k_moe_gemm), so either path can run any block. The same kernel also
+// runs the LM head of large passes (pages: model page, summary paragraph: greedy choice
+// over a 129,280-word vocabulary):
+//   LM:   per 256-row item and 256-column tile, the top-1/top-2 record of every row of
+//         A W_lm^T (float32 logits, never stored), merged later by k_argmax_reduce.
 #include "launch.h"
 
 namespace mv {
@@ -49,6 +53,7 @@ constexpr int kStageRuns = 16;         // runs per operand per stage
 constexpr int kLoadsPerStage = 4;      // direct loads per wavefront per stage
 constexpr int kUpStores = 8;           // epilogue stores per wavefront: UP 8 row tiles
 constexpr int kDownStores = 16;        //   DOWN 8 row tiles x 2 pairs
+constexpr int kLmStores = 1;           //   LM one merged record per lane
 
 // s_waitcnt for at most N vector-memory operations of this wavefront still in flight and
 // none of its LDS operations (expcnt left unconstrained).
@@ -81,15 +86,19 @@ __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0
 
 template <int EPI>
 __global__ __launch_bounds__(kTileThreads, 1) void k_moe_tiled(GemmArgs g) {
-  constexpr int NST = EPI == EPI_UP ? kUpStores : kDownStores;
+  constexpr int NST = EPI == EPI_UP ? kUpStores : (EPI == EPI_DOWN ? kDownStores : kLmStores);
   constexpr int STAGE2 = 2 * kLoadsPerStage;  // loads of two stages
   constexpr int WAVES = kTileThreads / kWave;
   __shared__ u32x4_t lds[kTileStages][2][kStageRuns * kRunUnits];
   // A source rows of this wavefront's two runs (lanes 0..15 run w, 16..31 run w + 8), for
   // the tiles of even and odd index
   __shared__ int rows_lds[2][WAVES][kWave];
+  // LM: the four column wavefronts' records of each row of the tile
+  __shared__ Top2 lm_red[EPI == EPI_LM ? 4 : 1][EPI == EPI_LM ? kTileM : 1];
   const int NT = (g.NQ + kTilePairs - 1) / kTilePairs;
-  const int n_tiles = *g.n_work * NT;
+  // LM: no work list, the items are the consecutive 256-row blocks of the Tn rows
+  const int n_items = EPI == EPI_LM ? (g.Tn + kTileM - 1) / kTileM : *g.n_work;
+  const int n_tiles = n_items * NT;
   // This workgroup's tiles: XCD x (hardware workgroups are dealt to the 8 XCDs in turn)
   // owns the x-th contiguous range of logical tiles, and its nbx workgroups take every
   // nbx-th tile of it, so at any time one XCD works on neighbouring tiles (the row
@@ -119,13 +128,20 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_moe_tiled(GemmArgs g) {
   };
   auto info = [&](int m) __attribute__((always_inline)) {
     const int lt = start + jx + m * nbx;
-    const int item = __builtin_amdgcn_readfirstlane(lt / NT);
-    // the work list is not written while the kernel runs: read it as constant memory
-    // (a scalar load, which the waits for the direct loads do not count)
-    typedef int i32x4_t __attribute__((ext_vector_type(4)));
-    typedef const __attribute__((address_space(4))) i32x4_t* const_work_ptr;
-    const i32x4_t it = ((const_work_ptr)(uintptr_t)g.work)[item];
-    return TileInfo{it[0], it[1], it[2], it[3], lt - item * NT};
+    if constexpr (EPI == EPI_LM) {
+      // column-tile major: the row items of one column tile are neighbours on one XCD and
+      // share its weight tile through L2
+      const int nt = __builtin_amdgcn_readfirstlane(lt / n_items), item = lt - nt * n_items;
+      return TileInfo{0, item * kTileM, min(kTileM, g.Tn - item * kTileM), item * kTileM, nt};
+    } else {
+      const int item = __builtin_amdgcn_readfirstlane(lt / NT);
+      // the work list is not written while the kernel runs: read it as constant memory
+      // (a scalar load, which the waits for the direct loads do not count)
+      typedef int i32x4_t __attribute__((ext_vector_type(4)));
+      typedef const __attribute__((address_space(4))) i32x4_t* const_work_ptr;
+      const i32x4_t it = ((const_work_ptr)(uintptr_t)g.work)[item];
+      return TileInfo{it[0], it[1], it[2], it[3], lt - item * NT};
+    }
   };
   // The A source rows of tile t into rows_lds[buf][w]: lane l < 32 holds the row of row
   // (w + 8*(l/16))*16 + l%16 of the item (rows past its end repeat its last row; their
@@ -195,45 +211,84 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_moe_tiled(GemmArgs g) {
   // instruction writes 16 positions x 64 contiguous bytes instead of 16 x 32 bytes twice.
   auto epilogue = [&](const TileInfo& t) __attribute__((always_inline)) {
     const int gq = lane >> 4;
+    if constexpr (EPI == EPI_LM) {
+      // Each lane folds its 16 logits of a row in increasing column order (a later equal
+      // value never wins), the four lane groups and then the four column wavefronts are
+      // merged (lowest index on equal values), and lane l < 32 of wavefront w stores row
+      // 32 w + l's record of this column tile. Every lane stores exactly once: lanes with
+      // no row of the item write the record slot past the last one.
+      const float NEG = -__builtin_huge_valf();
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = 128 * wm + 16 * i + (lane & 15);
-      const bool row_ok = r < t.M;
-      if constexpr (EPI == EPI_UP) {
-        uint32_t lo[2], hi[2];  // bf16 pairs of columns 4*gq, 4*gq+1 and 4*gq+2, 4*gq+3 of pair pp
-#pragma unroll
-        for (int pp = 0; pp < 2; ++pp) {
-          float sv[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) sv[j] = swiglu(acc[i][pp][0][j], acc[i][pp][1][j]);
-          lo[pp] = pack_bf16x2(sv[0], sv[1]);
-          hi[pp] = pack_bf16x2(sv[2], sv[3]);
-        }
-        // lane group gq now holds columns 8*(gq/2)..+7 of pair 2*wn + gq%2
-        const auto xl = __builtin_amdgcn_permlane16_swap(lo[0], lo[1], false, false);
-        const auto xh = __builtin_amdgcn_permlane16_swap(hi[0], hi[1], false, false);
-        const int q = t.nt * kTilePairs + 2 * wn + (gq & 1);
-        const int e = q * 16 + 8 * (gq >> 1);
-        const size_t off = row_ok && q < g.NQ ? (size_t)(t.row0 + r) * g.I + stage_ordered_elem(e)
-                                              : (size_t)g.sink_row * g.I;
-        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(g.h) + off) =
-            make_uint4((uint32_t)xl[0], (uint32_t)xh[0], (uint32_t)xl[1], (uint32_t)xh[1]);
-      } else {
+      for (int i = 0; i < 8; ++i) {
+        Top2 b{NEG, INT_MAX, NEG};
 #pragma unroll
         for (int pp = 0; pp < 2; ++pp) {
           const int q = t.nt * kTilePairs + 2 * wn + pp;
-          const uint32_t d0 = pack_bf16x2(acc[i][pp][0][0], acc[i][pp][0][1]);
-          const uint32_t d1 = pack_bf16x2(acc[i][pp][0][2], acc[i][pp][0][3]);
-          const uint32_t e0 = pack_bf16x2(acc[i][pp][1][0], acc[i][pp][1][1]);
-          const uint32_t e1 = pack_bf16x2(acc[i][pp][1][2], acc[i][pp][1][3]);
-          // lane group gq now holds columns 8*(gq/2)..+7 of the pair's tile gq%2
-          const auto x0 = __builtin_amdgcn_permlane16_swap(d0, e0, false, false);
-          const auto x1 = __builtin_amdgcn_permlane16_swap(d1, e1, false, false);
-          const int col = (2 * q + (gq & 1)) * 16 + 8 * (gq >> 1);
-          const size_t off = row_ok && q < g.NQ && col < g.H ? (size_t)(t.row0 + r) * g.H + col
-                                                             : (size_t)g.sink_row * g.H;
-          *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(g.ybuf) + off) =
-              make_uint4((uint32_t)x0[0], (uint32_t)x1[0], (uint32_t)x0[1], (uint32_t)x1[1]);
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int c = (2 * q + tt) * 16 + 4 * gq + j;
+              const float v = (q < g.NQ && c < g.n_valid) ? acc[i][pp][tt][j] : NEG;
+              const bool gt = v > b.v1;
+              b.v2 = gt ? b.v1 : fmaxf(b.v2, v);
+              b.i1 = gt ? c : b.i1;
+              b.v1 = gt ? v : b.v1;
+            }
+        }
+        b = top2_merge(b, top2_shfl_xor(b, 16));
+        b = top2_merge(b, top2_shfl_xor(b, 32));
+        if (lane < 16) lm_red[wn][128 * wm + 16 * i + lane] = b;
+      }
+      wait_vmem_lds<63>();  // this wavefront's LDS writes done (loads in flight stay)
+      block_barrier();
+      const int r = 32 * w + (lane & 31);
+      Top2 rec = lm_red[0][r];
+#pragma unroll
+      for (int v = 1; v < 4; ++v) rec = top2_merge(rec, lm_red[v][r]);
+      const size_t slot = lane < 32 && r < t.M ? (size_t)(t.row0 + r) * g.n_pg + t.nt : (size_t)g.Tn * g.n_pg;
+      g.part[slot] = rec;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = 128 * wm + 16 * i + (lane & 15);
+        const bool row_ok = r < t.M;
+        if constexpr (EPI == EPI_UP) {
+          uint32_t lo[2], hi[2];  // bf16 pairs of columns 4*gq, 4*gq+1 and 4*gq+2, 4*gq+3 of pair pp
+#pragma unroll
+          for (int pp = 0; pp < 2; ++pp) {
+            float sv[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sv[j] = swiglu(acc[i][pp][0][j], acc[i][pp][1][j]);
+            lo[pp] = pack_bf16x2(sv[0], sv[1]);
+            hi[pp] = pack_bf16x2(sv[2], sv[3]);
+          }
+          // lane group gq now holds columns 8*(gq/2)..+7 of pair 2*wn + gq%2
+          const auto xl = __builtin_amdgcn_permlane16_swap(lo[0], lo[1], false, false);
+          const auto xh = __builtin_amdgcn_permlane16_swap(hi[0], hi[1], false, false);
+          const int q = t.nt * kTilePairs + 2 * wn + (gq & 1);
+          const int e = q * 16 + 8 * (gq >> 1);
+          const size_t off = row_ok && q < g.NQ ? (size_t)(t.row0 + r) * g.I + stage_ordered_elem(e)
+                                                : (size_t)g.sink_row * g.I;
+          *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(g.h) + off) =
+              make_uint4((uint32_t)xl[0], (uint32_t)xh[0], (uint32_t)xl[1], (uint32_t)xh[1]);
+        } else {
+#pragma unroll
+          for (int pp = 0; pp < 2; ++pp) {
+            const int q = t.nt * kTilePairs + 2 * wn + pp;
+            const uint32_t d0 = pack_bf16x2(acc[i][pp][0][0], acc[i][pp][0][1]);
+            const uint32_t d1 = pack_bf16x2(acc[i][pp][0][2], acc[i][pp][0][3]);
+            const uint32_t e0 = pack_bf16x2(acc[i][pp][1][0], acc[i][pp][1][1]);
+            const uint32_t e1 = pack_bf16x2(acc[i][pp][1][2], acc[i][pp][1][3]);
+            // lane group gq now holds columns 8*(gq/2)..+7 of the pair's tile gq%2
+            const auto x0 = __builtin_amdgcn_permlane16_swap(d0, e0, false, false);
+            const auto x1 = __builtin_amdgcn_permlane16_swap(d1, e1, false, false);
+            const int col = (2 * q + (gq & 1)) * 16 + 8 * (gq >> 1);
+            const size_t off = row_ok && q < g.NQ && col < g.H ? (size_t)(t.row0 + r) * g.H + col
+                                                               : (size_t)g.sink_row * g.H;
+            *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(g.ybuf) + off) =
+                make_uint4((uint32_t)x0[0], (uint32_t)x1[0], (uint32_t)x0[1], (uint32_t)x1[1]);
+          }
         }
       }
     }
@@ -321,7 +376,8 @@ int tiled_tiles_per_item(int NQ) { return (NQ + kTilePairs - 1) / kTilePairs; }
 hipError_t launch_gemm_tiled(int epi, const GemmArgs& args, unsigned n_wg, hipStream_t stream) {
   const dim3 grid(n_wg), block(kTileThreads);
   if (epi == EPI_UP) k_moe_tiled<EPI_UP><<<grid, block, 0, stream>>>(args);
-  else k_moe_tiled<EPI_DOWN><<<grid, block, 0, stream>>>(args);
+  else if (epi == EPI_DOWN) k_moe_tiled<EPI_DOWN><<<grid, block, 0, stream>>>(args);
+  else k_moe_tiled<EPI_LM><<<grid, block, 0, stream>>>(args);
   return hipGetLastError();
 }
 

@@ -7,7 +7,10 @@
             --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR --copy-bytes N --out FILE
         per-launch HBM bytes of every kernel from two --pmc runs (FETCH_SIZE, then
         WRITE_SIZE; rocprofv3 csv output) of the bench, each scaled by what the same
-        counter reads for a plain copy of N bytes (--copy-calibration mode of bench.py).
+        counter reads for a plain copy of N bytes (--copy-calibration mode of bench.py);
+    python -m lossless_speculative_verification_amd.profiling mfma DIR
+        per-kernel MFMA-busy percentage and bf16 MFMA flop rate from one --pmc run with
+        MfmaUtil and SQ_INSTS_VALU_MFMA_MOPS_BF16 plus --kernel-trace (csv output).
 
 The traffic file records the sha256 of the kernel sources; bench.py reports a kernel's
 traffic only while that hash still matches the sources (counters of an older build
@@ -120,6 +123,54 @@ def read_traffic(path: str, kernel_prefix: str) -> Optional[dict]:
     return None
 
 
+def _col(row: dict, *names: str) -> str:
+    """The first column of a rocprofv3 csv row whose name matches one of names (case and
+    underscores ignored)."""
+    norm = {k.replace("_", "").lower(): k for k in row}
+    for n in names:
+        k = norm.get(n.replace("_", "").lower())
+        if k is not None:
+            return row[k]
+    raise KeyError(f"none of {names} in {sorted(row)}")
+
+
+def mfma_table(csv_dir: str, peak_flops: float = 2.5e15) -> str:
+    """Markdown table per kernel from one --pmc run with MfmaUtil and
+    SQ_INSTS_VALU_MFMA_MOPS_BF16 plus --kernel-trace (csv output): median MFMA-busy percentage
+    (busy cycles of the matrix units over active cycles of all SIMDs), bf16 MFMA flops per
+    launch (MOPS x 512), the launch's duration in that run, and the resulting rate against the
+    dense bf16 peak."""
+    cpaths = glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True)
+    tpaths = glob.glob(os.path.join(csv_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if not cpaths or not tpaths:
+        raise FileNotFoundError(f"need *counter_collection.csv and *kernel_trace.csv under {csv_dir}")
+    dur = {}
+    for p in tpaths:
+        with open(p) as f:
+            for r in csv.DictReader(f):
+                dur[_col(r, "Dispatch_Id")] = (float(_col(r, "End_Timestamp")) - float(_col(r, "Start_Timestamp"))) * 1e-9
+    per = collections.defaultdict(lambda: collections.defaultdict(dict))  # kernel -> dispatch -> counter -> value
+    for p in cpaths:
+        with open(p) as f:
+            for r in csv.DictReader(f):
+                d = _col(r, "Dispatch_Id")
+                per[short_name(_col(r, "Kernel_Name"))][d][_col(r, "Counter_Name")] = float(_col(r, "Counter_Value"))
+    out = ["| kernel | launches | MFMA busy % (median) | bf16 MFMA flops / launch | launch us (this run) | "
+           f"PFLOP/s | of {peak_flops / 1e15:.1f} PFLOP/s |", "|---|---|---|---|---|---|---|"]
+    rows = []
+    for k, ds in per.items():
+        util = [v.get("MfmaUtil") for v in ds.values() if v.get("MfmaUtil") is not None]
+        flops = [v["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 for v in ds.values() if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in v]
+        secs = [dur[d] for d in ds if d in dur]
+        if not flops or max(flops) == 0:
+            continue
+        f, t = statistics.median(flops), statistics.median(secs) if secs else float("nan")
+        rows.append((f * len(ds), f"| `{k[:60]}` | {len(ds)} | {statistics.median(util) if util else float('nan'):.1f} | "
+                                  f"{f:.4g} | {t * 1e6:.1f} | {f / t / 1e15:.3f} | {f / t / peak_flops:.3f} |"))
+    out += [r for _, r in sorted(rows, key=lambda x: -x[0])]
+    return "\n".join(out)
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -134,7 +185,12 @@ def main():
     r.add_argument("--copy-bytes", type=int, required=True)
     r.add_argument("--out", required=True)
     r.add_argument("--command", default="")
+    m = sub.add_parser("mfma")
+    m.add_argument("csv_dir")
     args = ap.parse_args()
+    if args.cmd == "mfma":
+        print(mfma_table(args.csv_dir))
+        return
     if args.cmd == "trace":
         print(trace_table(args.db))
         print()

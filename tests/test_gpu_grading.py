@@ -133,13 +133,16 @@ def _tie_model(V, T):
     return wl
 
 
-@pytest.mark.parametrize("V", [129280, 20010])  # 20,010: a last column pair with 10 real columns
-def test_lm_head_constructed_ties(V):
+# 20,010: a last column pair with 10 real columns; 448 and 512 positions: the LM head runs
+# on the tiled GEMM (256-row items of 256-column tiles; the second item of 448 is 3/4 full)
+# instead of the streaming kernel
+@pytest.mark.parametrize("V,T", [(129280, 136), (20010, 136), (129280, 448), (20010, 512)])
+def test_lm_head_constructed_ties(V, T):
     """Identical LM-head rows j1 < j2 (< j3) give bitwise equal logits: the argmax must be
     the lowest index and the margin exactly 0. Pairs sit in one lane, in one wavefront's
-    two column pairs, in two wavefronts of a workgroup, in different workgroups, at the
-    padded last column pair, and in the second 128-row block of positions."""
-    T = 136
+    two column pairs, in two wavefronts of a workgroup, in different workgroups (column
+    tiles), across the 512-column boundary, at the padded last column pair, and in the
+    second row block of positions."""
     wl = _tie_model(V, T)
     w = W.make_weights(wl)
     x = W.make_hidden(wl)
@@ -149,7 +152,7 @@ def test_lm_head_constructed_ties(V):
     ties = [(100, 101), (200, 232), (300, 480), (1000, V // 2), (5, last), (last - 2, last - 1), (7000, 8000, 9000),
             (64, 65, 96), (511, 512), (3, 4000)]
     assert len({j for js in ties for j in js}) == sum(len(js) for js in ties)  # no row planted twice
-    owners = list(range(8)) + [128, 135]
+    owners = list(range(8)) + [128, T - 1]
     planted = {}
     for t, js in zip(owners, ties):
         row = O.round_bf16(0.05 * np.sign(a[t]))  # logit 0.05 * sum |a| (about 51) for position t
