@@ -50,6 +50,17 @@ int64_t max_work_items(const moe_verify_config& c, int64_t T, int64_t mb = mv::k
   return (T * c.top_k + mb - 1) / mb + c.n_routed + (int64_t)c.n_shared * ((T + mb - 1) / mb);
 }
 
+// Split plan of tiled passes planned by one workgroup: routed experts with fewer than
+// kSplitHotRows rows go to the tiled kernel's streaming unit in items of kSplitRows rows
+// (a mostly empty 256 x 256 tile costs a compute unit as long as a full one, and the
+// streaming unit reads the expert's weights once per 32 rows instead). At most
+// ceil((kSplitHotRows - 1) / kSplitRows) items per routed expert.
+constexpr int kSplitHotRows = 64;
+constexpr int kSplitRows = 32;
+int64_t max_split_items(const moe_verify_config& c) {
+  return (int64_t)c.n_routed * ((kSplitHotRows - 1 + kSplitRows - 1) / kSplitRows);
+}
+
 // Passes of at least this many positions run the expert GEMMs on the LDS-tiled kernel
 // (bf16 weights, contractions of at least 256 elements): work items of up to kTileM rows
 // then keep the matrix cores busy, while smaller passes are bound by the weight stream
@@ -151,6 +162,8 @@ struct Workspace {
   int32_t* row_dst = nullptr;    // [P*k] position-major ybuf row of each routed row (streaming path)
   int4* work = nullptr;          // GEMM work list
   int32_t* n_work = nullptr;     // its length
+  int4* work2 = nullptr;         // split plan: streaming work items of the tiled passes
+  int32_t* n_work2 = nullptr;    // their number
   int32_t* chunk_cnt = nullptr;  // [chunks][64] expert counts per slot chunk (large-pass plan)
   void* h = nullptr;             // [P*(k+S)+1][I] SwiGLU rows (+ a sink row for padding stores)
   void* ybuf = nullptr;          // [P*(k+S)+1][H] expert outputs, one row per slot, weight type
@@ -180,6 +193,8 @@ size_t layout_workspace(const moe_verify_config& g, int n_pg_lm, int P, char* ba
   take(&o.row_dst, Pz * k * sizeof(int32_t));
   take(&o.work, (size_t)max_work_items(g, P) * sizeof(int4));
   take(&o.n_work, sizeof(int32_t));
+  take(&o.work2, (size_t)max_split_items(g) * sizeof(int4));
+  take(&o.n_work2, sizeof(int32_t));
   take(&o.chunk_cnt, (size_t)mv::plan_chunks(P, g.top_k) * 64 * sizeof(int32_t));
   take(&o.h, (Pz * KS + 1) * I * es);
   take(&o.ybuf, (Pz * KS + 1) * H * es);
@@ -325,6 +340,14 @@ int run_block(moe_verify_ctx* c, const Workspace& w, int l, const float* x_in, c
   pa.counts = w.counts + (size_t)l * E;
   pa.mb = mb;
   pa.chunk_cnt = w.chunk_cnt;
+  // tiled passes that one plan workgroup handles split off their cold experts
+  const bool split = tiled && mv::plan_chunks(Tn, k) <= mv::kPlanSingleMaxChunks;
+  if (split) {
+    pa.hot_rows = kSplitHotRows;
+    pa.mb2 = kSplitRows;
+    pa.work2 = w.work2;
+    pa.n_work2 = w.n_work2;
+  }
   c->prof_begin(MOE_PROF_NORM_ROUTE, st);
   MV_CHECK(mv::launch_norm_route(g.wdtype, true, x_in, ybuf_prev, w.slot_row, x_out, nullptr, w.a,
                                  c->router_p + l * c->router_units_per_layer, c->bias_p + (size_t)l * 64, w.topk_id,
@@ -352,6 +375,10 @@ int run_block(moe_verify_ctx* c, const Workspace& w, int l, const float* x_in, c
   a.plan_counts = pa.counts;
   a.plan_row_dst = w.row_dst;
   a.mb = mb;
+  if (split) {
+    a.work2 = w.work2;
+    a.n_work2 = w.n_work2;
+  }
   // Streaming kernel: two pairs per wavefront when the expected items x pairs fill at
   // least one round of resident wavefronts (routed items: one per touched expert while
   // positions are few).

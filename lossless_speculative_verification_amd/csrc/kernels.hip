@@ -23,6 +23,7 @@
 #include <climits>
 
 #include "launch.h"
+#include "stream_gemm.h"
 
 namespace mv {
 
@@ -653,11 +654,55 @@ __device__ void write_work(const PlanArgs& pa, const int* off, const int* wstart
   if (tid == 0) *pa.n_work = nsw + wstart[64];
 }
 
+// Split plan (pa.hot_rows > 0): wavefront 0, lane = expert with c rows: items of a hot
+// expert (c >= hot_rows) in the tiled list (first items wstart), of a cold one in the
+// streaming list (first items wstart2, mb2 rows each).
+__device__ void split_starts(const PlanArgs& pa, int c, int* wstart, int* wstart2) {
+  const int lane = threadIdx.x & 63;
+  const bool hot = c >= pa.hot_rows;
+  const int nb = hot ? (c + pa.mb - 1) / pa.mb : 0, nb2 = hot ? 0 : (c + pa.mb2 - 1) / pa.mb2;
+  int sn = nb, sn2 = nb2;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(sn, d, kWave), o2 = __shfl_up(sn2, d, kWave);
+    if (lane >= d) { sn += o; sn2 += o2; }
+  }
+  wstart[lane] = sn - nb;
+  wstart2[lane] = sn2 - nb2;
+  if (lane == 63) { wstart[64] = sn; wstart2[64] = sn2; }
+}
+
+__device__ void write_work_split(const PlanArgs& pa, const int* off, const int* wstart, const int* wstart2,
+                                 int nthreads) {
+  const int tid = threadIdx.x, mb = pa.mb, mb2 = pa.mb2, Tn = pa.Tn, N = pa.Tn * pa.k;
+  const int mbT = (Tn + mb - 1) / mb;
+  const int nsw = pa.S * mbT;  // shared-expert items come first
+  for (int idx = tid; idx < nsw; idx += nthreads) {
+    const int s = idx / mbT, b = idx - s * mbT;
+    pa.work[idx] = make_int4(pa.E + s, N + s * Tn + b * mb, min(mb, Tn - b * mb), b * mb);
+  }
+  for (int e = tid; e < pa.E; e += nthreads) {  // one thread per expert
+    const int c = off[e + 1] - off[e];
+    if (c >= pa.hot_rows) {
+      for (int b = 0; b * mb < c; ++b)
+        pa.work[nsw + wstart[e] + b] = make_int4(e, off[e] + b * mb, min(mb, c - b * mb), 0);
+    } else {
+      for (int b = 0; b * mb2 < c; ++b)
+        pa.work2[wstart2[e] + b] = make_int4(e, off[e] + b * mb2, min(mb2, c - b * mb2), 0);
+    }
+  }
+  if (tid == 0) {
+    *pa.n_work = nsw + wstart[64];
+    *pa.n_work2 = wstart2[64];
+  }
+}
+
 __global__ __launch_bounds__(1024) void k_plan(PlanArgs pa) {
   constexpr int NW = 16;
   __shared__ int hist[NW][64];
   __shared__ int off[65];
   __shared__ int wstart[65];
+  __shared__ int wstart2[65];
   const int N = pa.Tn * pa.k;
   seg_hist<NW>(pa, 0, N, hist);
   if (threadIdx.x < kWave) {
@@ -665,11 +710,13 @@ __global__ __launch_bounds__(1024) void k_plan(PlanArgs pa) {
     if ((int)threadIdx.x < pa.E)
       for (int w = 0; w < NW; ++w) c += hist[w][threadIdx.x];
     expert_offsets(pa, c, off, wstart, true);
+    if (pa.hot_rows > 0) split_starts(pa, (int)threadIdx.x < pa.E ? c : 0, wstart, wstart2);
     seg_cursors<NW>(hist, off[threadIdx.x]);
   }
   __syncthreads();
   seg_scatter<NW>(pa, 0, N, hist);
-  write_work(pa, off, wstart, NW * kWave);
+  if (pa.hot_rows > 0) write_work_split(pa, off, wstart, wstart2, NW * kWave);
+  else write_work(pa, off, wstart, NW * kWave);
 }
 
 // Large pass, step 1: chunk c's routed-slot count per expert -> chunk_cnt[c][64].
@@ -714,157 +761,6 @@ __global__ __launch_bounds__(256) void k_plan_scatter(PlanArgs pa) {
 }
 
 // ============================================================================ grouped MFMA GEMM
-
-// One wavefront computes PPW consecutive column pairs (2 x 16 output columns each) of one
-// expert work item (up to 16*NMT rows) over the whole contraction, the pairs side by
-// side so that one loop serves them all:
-//  * weights stream from HBM once, in the pair layout: per 256-byte K block and pair,
-//    8 fully coalesced 1 KB non-temporal loads; D K blocks in flight;
-//  * the item's activation rows are read straight from global memory (small and
-//    L2-resident), once per K block for all PPW pairs: lane l reads row 16*mt + l%16
-//    of each row tile, the 64 bytes of the K block that its lane group l/16 contracts;
-//    rows past the item's end repeat row 0 and their results are dropped;
-//  * products accumulate in float32 MFMA (16x16x32 bf16, or 16x16x4 f32).
-// The main loop holds only loads and MFMAs, and no load in it depends on a branch: a
-// store, a spill or a conditional load there would make the compiler wait for every
-// load in flight. The epilogue follows the loop:
-//   UP:   tile t = 0 is the gate projection, t = 1 the up projection of the same 16
-//         intermediate columns; the epilogue forms silu(gate) * up and stores it.
-//   DOWN: the epilogue writes the row's expert output to its slot's position-major row
-//         of ybuf, t*(k+S) + j (the gate is applied where the slots are summed); no two
-//         wavefronts write the same element.
-// There is no LDS and no barrier: wavefronts run free.
-template <typename T, int EPI, int NMT, int PPW, int D>
-__device__ __forceinline__ void moe_stream(const GemmArgs& g, int e, int row0, int M, int tok0, int q0,
-                                           const int* tok_lds = nullptr) {
-  const int lane = threadIdx.x & 63;
-  const int row_units = g.K * (int)sizeof(T) / 16;
-  const int NKB = row_units / kChunksPerRow;
-  const int col = lane & 15, rg = (lane >> 4) * 4;
-  const uint4* Bw[PPW];
-#pragma unroll
-  for (int p = 0; p < PPW; ++p) {
-    const int q = min(q0 + p, g.NQ - 1);  // a pair past the end repeats the last one; not stored
-    Bw[p] = g.B + ((size_t)e * g.NQ + q) * (size_t)NKB * kPairUnits + lane;
-  }
-  uint4 ra[D][NMT][4], rb[D][PPW][8];
-  f32x4_t acc[PPW][NMT][2];
-#pragma unroll
-  for (int p = 0; p < PPW; ++p)
-#pragma unroll
-    for (int mt = 0; mt < NMT; ++mt) acc[p][mt][0] = acc[p][mt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  int kl = 0;  // next K block to load (stays at the last one once reached, when NKB < D)
-  auto load_w = [&](uint4(&b)[PPW][8]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int p = 0; p < PPW; ++p)
-#pragma unroll
-      for (int u = 0; u < 8; ++u) b[p][u] = load_stream(Bw[p] + (size_t)kl * kPairUnits + u * kWave);
-  };
-  // The first weight blocks go out before anything that needs the item's row indices.
-  static_for<D>([&](auto sc) __attribute__((always_inline)) {
-    load_w(rb[decltype(sc)::value]);
-    kl += kl < NKB - 1 ? 1 : 0;
-  });
-
-  const uint4* ap[NMT];
-#pragma unroll
-  for (int mt = 0; mt < NMT; ++mt) {
-    const int r = mt * 16 + (lane & 15);
-    const int rr = r < M ? r : 0;
-    int src;
-    if constexpr (EPI == EPI_UP) src = (e < g.E) ? (tok_lds ? tok_lds[rr] : g.row_tok[row0 + rr]) : tok0 + rr;
-    else src = row0 + rr;
-    ap[mt] = reinterpret_cast<const uint4*>(g.A) + (size_t)src * row_units + (lane >> 4) * 4;
-  }
-  // DOWN: lane l holds the position-major ybuf row of item row l % (16*NMT); routed rows
-  // from the plan, shared expert s's row of position t is t*KS + k + s
-  int dst_row = 0;
-  if constexpr (EPI == EPI_DOWN) {
-    const int r = lane & (16 * NMT - 1);
-    const int rr = r < M ? r : 0;
-    dst_row = e < g.E ? g.row_dst[row0 + rr] : (tok0 + rr) * g.KS + g.k + (e - g.E);
-  }
-  int ka = 0;  // next K block of activations to load
-  auto load_a = [&](uint4(&a)[NMT][4]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) a[mt][s] = ap[mt][ka * kChunksPerRow + s];
-    ka += ka < NKB - 1 ? 1 : 0;
-  };
-  static_for<D>([&](auto sc) __attribute__((always_inline)) { load_a(ra[decltype(sc)::value]); });
-  // In the loop a stage's activations go out before its weights.
-  auto load = [&](uint4(&a)[NMT][4], uint4(&b)[PPW][8]) __attribute__((always_inline)) {
-    load_a(a);
-    load_w(b);
-    kl += kl < NKB - 1 ? 1 : 0;
-  };
-  auto compute = [&](const uint4(&a)[NMT][4], const uint4(&b)[PPW][8]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int p = 0; p < PPW; ++p)
-#pragma unroll
-        for (int mt = 0; mt < NMT; ++mt) {
-          mma_chunk(acc[p][mt][0], a[mt][s], b[p][s], (T*)nullptr);
-          mma_chunk(acc[p][mt][1], a[mt][s], b[p][4 + s], (T*)nullptr);
-        }
-  };
-
-  // Main loop: every load in it is in range (K block k0 + D + s < NKB). The tail then
-  // computes the last D..2D-1 blocks, loading the r = NKB - k0 - D not yet requested.
-  int k0 = 0;
-  for (; k0 + 2 * D <= NKB; k0 += D) {
-    static_for<D>([&](auto sc) __attribute__((always_inline)) {
-      constexpr int s = decltype(sc)::value;
-      compute(ra[s], rb[s]);
-      load(ra[s], rb[s]);
-      __builtin_amdgcn_sched_barrier(0);  // keep the loads here, D blocks ahead of their use
-    });
-  }
-  const int r = NKB - k0 - D;
-  static_for<D>([&](auto sc) __attribute__((always_inline)) {
-    constexpr int s = decltype(sc)::value;
-    if (k0 + s < NKB) compute(ra[s], rb[s]);
-    if (s < r) load(ra[s], rb[s]);
-  });
-  static_for<D - 1>([&](auto sc) __attribute__((always_inline)) {
-    constexpr int s = decltype(sc)::value;
-    if (s < r) compute(ra[s], rb[s]);
-  });
-
-#pragma unroll
-  for (int p = 0; p < PPW; ++p) {
-    const int q = q0 + p;
-    if (q >= g.NQ) break;
-    if constexpr (EPI == EPI_UP) {
-      T* h = reinterpret_cast<T*>(g.h);
-#pragma unroll
-      for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = mt * 16 + rg + i;
-          if (r < M) {
-            const float gv = acc[p][mt][0][i], uv = acc[p][mt][1][i];
-            store_elem(h, (size_t)(row0 + r) * g.I + q * 16 + col, swiglu(gv, uv));
-          }
-        }
-    } else {
-#pragma unroll
-      for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = mt * 16 + rg + i;
-          const int dr = __shfl(dst_row, r, kWave);
-          if (r < M) {
-            T* yrow = reinterpret_cast<T*>(g.ybuf) + (size_t)dr * g.H + (2 * q) * 16 + col;
-            store_elem(yrow, 0, acc[p][mt][0][i]);
-            store_elem(yrow, 16, acc[p][mt][1][i]);
-          }
-        }
-    }
-  }
-}
 
 // Expert GEMM over the device-built work list, PPW = g.ppw pairs per wavefront (chosen
 // on the host from the position count). Exactly the workgroups that carry work come
@@ -1386,6 +1282,7 @@ int plan_chunks(int Tn, int k) { return (Tn * k + kPlanChunk - 1) / kPlanChunk; 
 
 hipError_t launch_plan(const PlanArgs& pa, hipStream_t stream) {
   const int n = plan_chunks(pa.Tn, pa.k);
+  if (pa.hot_rows > 0 && n > kPlanSingleMaxChunks) return hipErrorInvalidValue;  // split plan: one workgroup only
   if (n <= kPlanSingleMaxChunks || !pa.chunk_cnt) {
     k_plan<<<1, 1024, 0, stream>>>(pa);
   } else {

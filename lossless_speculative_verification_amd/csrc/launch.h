@@ -23,6 +23,13 @@ struct PlanArgs {
   int32_t* counts;
   int mb;              // rows per work item
   int32_t* chunk_cnt;  // [chunks][64] scratch of the large-pass plan, or NULL (one workgroup)
+  // Split plan (one-workgroup plan only; hot_rows > 0): routed experts with fewer than
+  // hot_rows rows get work items of mb2 rows in a second list (work2 / n_work2) for the
+  // streaming unit of the tiled kernel; the others and the shared experts stay in work.
+  int hot_rows;
+  int mb2;
+  int4* work2;
+  int32_t* n_work2;
 };
 
 // Arguments of the expert GEMMs and the LM head (see k_moe_gemm, k_lm_head in kernels.hip).
@@ -50,6 +57,9 @@ struct GemmArgs {
   // topk_id and writes the work list, item count, per-expert counts and row_dst that the
   // plan kernel would have written (for the down GEMM and the bench), with items of mb rows.
   const int32_t* topk_id;
+  // Tiled kernel: streaming work items (split plan) run beside the tiles, or n_work2 NULL
+  const int4* work2;
+  const int32_t* n_work2;
   int4* plan_work;
   int32_t* plan_n_work;
   int32_t* plan_counts;

@@ -12,6 +12,7 @@
 //   LM:   per 256-row item and 256-column tile, the top-1/top-2 record of every row of
 //         A W_lm^T (float32 logits, never stored), merged later by k_argmax_reduce.
 #include "launch.h"
+#include "stream_gemm.h"
 
 namespace mv {
 
@@ -109,7 +110,8 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_moe_tiled(GemmArgs g) {
   for (int y = 0; y < x; ++y) start += (n_tiles - y + 7) >> 3;
   const int cnt = (n_tiles - x + 7) >> 3;
   const int n_my = jx < cnt ? (cnt - jx + nbx - 1) / nbx : 0;
-  if (n_my == 0) return;  // workgroup-uniform
+  do {  // the tiles of this workgroup (none: straight to the streaming items)
+  if (n_my == 0) break;  // workgroup-uniform
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -366,6 +368,48 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_moe_tiled(GemmArgs g) {
         if (m + 1 < n_my) nxt = info(m + 1);
       }
     });
+  }
+  } while (0);
+
+  // Streaming work items of a split plan (cold experts, items of up to 32 rows): one
+  // wavefront per (item, column pair) unit, no LDS and no barrier. Workgroups
+  // without tiles take the first round of units, then every workgroup takes units in
+  // turn (those without tiles first), so the units fill the compute units the tiles
+  // leave idle before they wait behind tiles.
+  if constexpr (EPI != EPI_LM) {
+    if (g.n_work2 != nullptr) {
+      const int units = *g.n_work2 * g.NQ;  // one column pair per unit
+      const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+      // workgroups without tiles (n_free; this one's index among them f, else its index
+      // among those with tiles t_idx), from the same per-XCD dealing as the tiles
+      int n_free = 0, f = -1, t_idx = 0;
+      for (int y = 0; y < 8; ++y) {
+        const int nb_y = ((int)gridDim.x - y + 7) >> 3, c_y = (n_tiles - y + 7) >> 3;
+        if (y == x) {
+          if (jx >= c_y) f = n_free + (jx - c_y);
+          else t_idx += jx;
+        }
+        if (y < x) t_idx += min(nb_y, c_y);
+        n_free += max(0, nb_y - c_y);
+      }
+      // this wavefront's units: u0 (tile-free workgroups' round 0), then u1, u1 + G8, ...
+      const int G8 = (int)gridDim.x * 8;
+      int u0, u1;
+      if (n_free == 0) {
+        u0 = units;
+        u1 = (int)blockIdx.x * 8 + wv;
+      } else {
+        // place in the order of all wavefronts, tile-free workgroups first
+        const int slot = f >= 0 ? f * 8 + wv : (n_free + t_idx) * 8 + wv;
+        u0 = f >= 0 ? slot : units;
+        u1 = n_free * 8 + slot;
+      }
+      for (int u = u0 < units ? u0 : u1; u < units; u = (u == u0 ? u1 : u + G8)) {
+        const int item = u / g.NQ, q = u - item * g.NQ;
+        const int4 it = g.work2[item];
+        moe_stream<uint16_t, EPI, 2, 1, MV_GEMM_D + 1, true>(g, it.x, it.y, it.z, it.w, q);
+      }
+    }
   }
 }
 
