@@ -294,3 +294,51 @@ def test_skewed_debug_layer_all_rows(name, layer):
     hot = float(np.isin(ref["ids"], np.arange(wl.n_biased)).mean())
     log(f"  {name} layer {layer}: decisive {dec.sum()}/{wl.positions}, m rel err {err:.2e}, hot share {hot:.3f}")
     assert err <= TOL["bf16"] and dec.sum() >= 0.8 * wl.positions
+
+
+# ----------------------------------------------------------------------------- tiled paths at their edges
+
+
+def test_split_plan_with_every_workgroup_tiled():
+    """2,048 positions with 8 hot experts (bias +1.6): the tiles (hot and shared experts)
+    exceed one round of compute units, so every workgroup runs streaming items of the cold
+    experts (fewer than 64 rows each) after its tiles; one block on every row."""
+    wl = WL["skewed70_b128_k3"].with_(name="split_full_t2048", n_layers=1, vocab=0, batch=2048, drafts=0,
+                                      bias_value=1.6)
+    x = W.make_hidden(wl)
+    ref = O.moe_layer(wl, host_weights(wl), 0, x)
+    counts = np.bincount(ref["ids"].ravel(), minlength=wl.n_routed)
+    cold = int((counts[wl.n_biased:] < 64).sum())
+    log(f"  cold experts (< 64 rows): {cold} of {wl.n_routed - wl.n_biased}; hot rows {counts[:wl.n_biased].min()}+")
+    assert cold >= 40 and counts[: wl.n_biased].min() > 512  # both lists in use, tiles beyond one round
+    m, tid, tw = run_debug_layer(wl, 0, x)
+    dec = ref["gap"] > GATE
+    np.testing.assert_array_equal(tid[dec], ref["ids"][dec])
+    assert np.abs(tw[dec] - ref["gates"][dec]).max() < 1e-3
+    err = row_rel_err(m[dec], ref["m"][dec])
+    log(f"  decisive {dec.sum()}/{wl.positions}, m rel err {err:.2e}")
+    assert err <= TOL["bf16"] and dec.sum() >= 0.8 * wl.positions
+
+
+@pytest.mark.parametrize("T", [256, 512, 700])
+def test_tiled_lm_head_small_model(T):
+    """The tiled LM head with the shortest contraction it takes (hidden 256: eight steps per
+    tile) and a vocabulary of 1,000 (four column tiles, the last one partial), against the
+    oracle's full-logit argmax; 700 rows: a second item three quarters full."""
+    wl = WL["layer1_bf16"].with_(name=f"lm_small_t{T}", hidden=256, inter=256, n_routed=8, top_k=2, n_shared=1,
+                                 vocab=1000, n_layers=1, batch=T, drafts=0)
+    w = W.make_weights(wl)
+    x = W.make_hidden(wl)
+    a = O.final_norm(wl, x)
+    ref_ids, ref_margin, _ = O.lm_head_argmax(a, w.lm_head, "bf16")
+    dw = bnd.upload_weights(w, DEV)
+    c = bnd.MoeVerify(wl, dw, T)
+    del dw
+    ids, margin = _head(wl, x, c)
+    dec = ref_margin > GATE
+    np.testing.assert_array_equal(ids[dec], ref_ids[dec])
+    assert np.all((ids >= 0) & (ids < wl.vocab))
+    assert np.abs(margin[dec] - ref_margin[dec]).max() < 2e-2
+    log(f"  decisive {dec.sum()}/{T} exact")
+    assert dec.sum() >= 0.8 * T
+    c.close()
