@@ -160,19 +160,26 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_moe_tiled(GemmArgs g) {
   // Stage st of tile t (rows src0/src1 of its two A runs): B from the tile's pairs (pairs
   // past the last repeat it; not stored). Wavefront-uniform base plus a 32-bit per-lane
   // offset (every operand buffer is below 4 GiB).
-  auto issue = [&](const TileInfo& t, int src0, int src1, int stage) __attribute__((always_inline)) {
+  auto issue_a = [&](int src0, int src1, int stage) __attribute__((always_inline)) {
     const int kb = stage >> 2, s = stage & 3, slot = stage & (kTileStages - 1);
     const uint32_t ka = (uint32_t)(((lane >> 4) + kb * kChunksPerRow + 4 * s) * 16);
+    lds_load16(Ab + ((uint32_t)src0 * row_bytes + ka), &lds[slot][0][w * kRunUnits]);
+    lds_load16(Ab + ((uint32_t)src1 * row_bytes + ka), &lds[slot][0][(w + 8) * kRunUnits]);
+  };
+  auto issue_b = [&](const TileInfo& t, int stage) __attribute__((always_inline)) {
+    const int kb = stage >> 2, s = stage & 3, slot = stage & (kTileStages - 1);
     const int q0 = min(t.nt * kTilePairs + (w >> 1), g.NQ - 1);
     const int q1 = min(t.nt * kTilePairs + ((w + 8) >> 1), g.NQ - 1);
     const size_t bk = (size_t)kb * kPairUnits + s * kWave + (w & 1) * 4 * kWave;
     const size_t b0 = ((size_t)t.e * g.NQ + q0) * (size_t)NKB * kPairUnits + bk;
     const size_t b1 = ((size_t)t.e * g.NQ + q1) * (size_t)NKB * kPairUnits + bk;
     const uint32_t lo = (uint32_t)lane * 16u;
-    lds_load16(Ab + ((uint32_t)src0 * row_bytes + ka), &lds[slot][0][w * kRunUnits]);
     lds_load16(Bb + b0 * 16 + lo, &lds[slot][1][w * kRunUnits]);
-    lds_load16(Ab + ((uint32_t)src1 * row_bytes + ka), &lds[slot][0][(w + 8) * kRunUnits]);
     lds_load16(Bb + b1 * 16 + lo, &lds[slot][1][(w + 8) * kRunUnits]);
+  };
+  auto issue = [&](const TileInfo& t, int src0, int src1, int stage) __attribute__((always_inline)) {
+    issue_a(src0, src1, stage);
+    issue_b(t, stage);
   };
 
   const int wm = w >> 2, wn = w & 3;
@@ -296,21 +303,28 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_moe_tiled(GemmArgs g) {
     }
   };
 
-  // prologue: tile 0's rows (waited for here), stages 0..2 requested; once stage 0 is in,
-  // stage 3 too, and stage 0 read
+  // prologue: tile 0's rows requested, then the weights of stages 0..2 (they need no row
+  // index, so they are in flight while the rows arrive); once the rows are in, the
+  // activations of stages 0..2; once stage 0 is in, stage 3 too, and stage 0 read; then
+  // the wait for stage 1 that the first step expects (its count assumes whole stages
+  // issued in order, which the prologue's split order is not)
   TileInfo cur = info(0), nxt = cur;
   if (n_my > 1) nxt = info(1);
   set_rows(cur, 0);
-  wait_vmem_lds<0>();
+  issue_b(cur, 0);
+  issue_b(cur, 1);
+  issue_b(cur, 2);
+  wait_vmem_lds<6>();  // the rows' load (before the six weight loads) is in
   int src0 = rows_lds[0][w][lane & 15], src1 = rows_lds[0][w][16 + (lane & 15)];
   clear();
-  issue(cur, src0, src1, 0);
-  issue(cur, src0, src1, 1);
-  issue(cur, src0, src1, 2);
-  wait_vmem_lds<STAGE2>();  // stage 0 in
+  issue_a(src0, src1, 0);
+  issue_a(src0, src1, 1);
+  issue_a(src0, src1, 2);
+  wait_vmem_lds<4>();  // stage 0 in: its activations, and everything issued before them
   block_barrier();
   issue(cur, src0, src1, 3);
   read(fa[0], fb[0], 0);
+  wait_vmem_lds<6>();  // stage 1 in: after its activations only stage 2's (2) and stage 3 (4)
 
   // Step gs (tile m, step st of it): wait for this wavefront's loads of stage gs + 1 (the
   // loads issued after them may stay in flight: two stages, plus the previous tile's
