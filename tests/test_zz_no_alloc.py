@@ -26,7 +26,9 @@ def _pass(c, wl, x, B, K, static):
     return ids.cpu().numpy(), margin.cpu().numpy(), hout.cpu().numpy()
 
 
-@pytest.mark.parametrize("name", ["decode_b32_k3", "layer1_bf16"])
+# skewed_b128_k3: 512 positions (tiled expert GEMM with the split plan, tiled LM head), then
+# 128 (streaming kernels) on the same array
+@pytest.mark.parametrize("name", ["decode_b32_k3", "layer1_bf16", "skewed_b128_k3"])
 def test_static_step_equals_step_on_two_calls(name):
     wl = W.WORKLOADS[name]
     c = context(wl)
