@@ -175,7 +175,9 @@ def test_small_bf16_both_gemm_paths(T):
     _check_step(wl, full, None, None, hout, x, min_decisive=T // 4)
 
 
-@pytest.mark.parametrize("B,K", [(75, 3), (300, 0)])
+# 300 positions: streaming LM head; 256 and 448: the tiled LM head (items of 256 rows, the
+# second 3/4 full), with the split plan's cold experts (fewer than 64 rows) among 16
+@pytest.mark.parametrize("B,K", [(75, 3), (300, 0), (64, 3), (112, 3)])
 def test_small_bf16_step_with_lm_head(B, K):
     """H = 512 with a 1000-token LM head, through the tiled expert kernel (>= 256
     positions): greedy ids exact on decisive positions, acceptance exact."""
