@@ -262,7 +262,8 @@ enum {
 
 /* Turn per-launch timing on (1) or off (0) and clear the totals. While on, every
  * moe_verify_step records a HIP event before and after each kernel launch on its stream
- * (do not capture such steps in a graph). Events are created here, not in the step. */
+ * (do not capture such steps in a graph). Events are created here, not in the step, as
+ * timing-only events without a system-scope fence. */
 int moe_verify_profile(moe_verify_ctx *ctx, int enable);
 
 /* Wait for the last profiled step, add its per-launch durations to the totals, and copy

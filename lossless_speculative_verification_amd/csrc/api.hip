@@ -870,7 +870,9 @@ MV_API int moe_verify_profile(moe_verify_ctx* c, int enable) {
   const size_t need = 2 * (size_t)(4 * c->cfg.n_layers + 3);
   while (enable && c->ev.size() < need) {
     hipEvent_t e;
-    MV_CHECK(hipEventCreate(&e));
+    // timing only: no system-scope fence at each record (its cache write-back and
+    // invalidate would otherwise be counted into the launches around it)
+    MV_CHECK(hipEventCreateWithFlags(&e, hipEventDisableSystemFence));
     c->ev.push_back(e);
   }
   c->ev_kind.assign(c->ev.size() / 2 + 1, 0);

@@ -11,6 +11,8 @@
 // over a 129,280-word vocabulary):
 //   LM:   per 256-row item and 256-column tile, the top-1/top-2 record of every row of
 //         A W_lm^T (float32 logits, never stored), merged later by k_argmax_reduce.
+// With a split plan (cold experts in a second work list of 32-row items) the kernel also
+// runs those items with the streaming unit, on compute units without tiles first.
 #include "launch.h"
 #include "stream_gemm.h"
 
@@ -34,8 +36,8 @@ namespace mv {
 //
 // The MFMA takes the weights as its first operand and the activations as its second, so
 // lane l of a 16x16 result holds position 16*i + l % 16 and the four consecutive output
-// columns 4*(l/16)..+3: the epilogue stores 8 bytes (four bf16) per lane and row, no LDS
-// round trip.
+// columns 4*(l/16)..+3; the epilogue pairs two such results with one lane swap and stores
+// 16 bytes per lane, no LDS round trip.
 //
 // Pipeline: kTileStages = 4 LDS stages in a ring. Step st multiplies stage st from
 // registers while stage st + 1's operands are read from LDS and stages st + 2 .. st + 4

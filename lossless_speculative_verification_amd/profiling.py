@@ -65,27 +65,35 @@ def trace_table(db_path: str) -> str:
 
 
 def step_breakdown(db_path: str, marker: str = "k_accept") -> str:
-    """Per-kernel medians within whole verify steps (a step ends with the acceptance kernel)."""
+    """Per-kernel medians within whole verify steps (a step ends with the acceptance kernel),
+    one table per pass shape: steps are grouped by their kernel count and the grid of their
+    first kernel (the routing norm's grid follows the number of positions)."""
     db = sqlite3.connect(db_path)
-    rows = db.execute("select name, start, end from kernels order by start").fetchall()
+    rows = db.execute("select name, start, end, grid_x from kernels order by start").fetchall()
     acc = [i for i, r in enumerate(rows) if short_name(r[0]).startswith(marker)]
     steps = [rows[a + 1:b + 1] for a, b in zip(acc[:-1], acc[1:])]
     if not steps:
         return "(no complete steps in the trace)"
-    n = collections.Counter(len(s) for s in steps).most_common(1)[0][0]
-    steps = [s for s in steps if len(s) == n]
-    durs = collections.defaultdict(list)
+    groups = collections.defaultdict(list)
     for s in steps:
-        for name, a, b in s:
-            durs[short_name(name)].append((b - a) / 1000.0)
-    spans = [(s[-1][2] - s[0][1]) / 1000.0 for s in steps]
-    out = [f"{len(steps)} steps of {n} kernels; step span median {statistics.median(spans):.1f} us "
-           f"(first kernel start to acceptance end)", "",
-           "| kernel | launches/step | median us | us/step |", "|---|---|---|---|"]
-    for k, v in durs.items():
-        per = len(v) // len(steps)
-        out.append(f"| `{k[:60]}` | {per} | {statistics.median(v):.2f} | {sum(v) / len(steps):.1f} |")
-    return "\n".join(out)
+        groups[(len(s), s[0][3])].append(s)
+    out = []
+    for (n, grid), ss in sorted(groups.items(), key=lambda kv: -len(kv[1])):
+        if len(ss) < 3:
+            continue
+        durs = collections.defaultdict(list)
+        for s in ss:
+            for name, a, b, _ in s:
+                durs[short_name(name)].append((b - a) / 1000.0)
+        spans = [(s[-1][2] - s[0][1]) / 1000.0 for s in ss]
+        out += [f"{len(ss)} steps of {n} kernels, first kernel grid {grid} threads; step span median "
+                f"{statistics.median(spans):.1f} us (first kernel start to acceptance end)", "",
+                "| kernel | launches/step | median us | us/step |", "|---|---|---|---|"]
+        for k, v in durs.items():
+            per = len(v) // len(ss)
+            out.append(f"| `{k[:60]}` | {per} | {statistics.median(v):.2f} | {sum(v) / len(ss):.1f} |")
+        out.append("")
+    return "\n".join(out).rstrip() if out else "(no complete steps in the trace)"
 
 
 def counter_medians(csv_dir: str) -> Dict[str, float]:
