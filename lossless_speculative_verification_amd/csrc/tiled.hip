@@ -203,9 +203,10 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_moe_tiled(GemmArgs g) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) a[i] = lds[slot][0][(8 * wm + i) * kRunUnits + lane];
   };
-  auto mma = [&](const u32x4_t(&a)[8], const u32x4_t(&b)[2][2]) __attribute__((always_inline)) {
+  // the 8 products of row tiles i0 and i0 + 1
+  auto mma_rows = [&](const u32x4_t(&a)[8], const u32x4_t(&b)[2][2], int i0) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = i0; i < i0 + 2; ++i)
 #pragma unroll
       for (int pp = 0; pp < 2; ++pp)
 #pragma unroll
@@ -330,10 +331,11 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_moe_tiled(GemmArgs g) {
 
   // Step gs (tile m, step st of it): wait for this wavefront's loads of stage gs + 1 (the
   // loads issued after them may stay in flight: two stages, plus the previous tile's
-  // stores in the first three steps of a tile) and for its LDS reads, barrier, read stage
-  // gs + 1's operands and the A rows of the stage to request, multiply stage gs, then
-  // request stage gs + 4 into the slot stage gs freed. The scheduling fences keep that
-  // order (the compiler would otherwise pull each read next to its first use). At step 0
+  // stores in the first three steps of a tile) and for its LDS reads, barrier, then
+  // multiply stage gs while reading stage gs + 1's operands and the A rows of the stage to
+  // request, and request stage gs + 4 into the slot stage gs freed. The scheduling fences
+  // keep that order (the compiler would otherwise pull each read next to its first use,
+  // and move the requests). At step 0
   // of tile m the rows of tile m + 1 are set (in by step 3, before its first request);
   // the last step of a tile ends with its epilogue.
   int m = 0, st = 0;
@@ -356,24 +358,54 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_moe_tiled(GemmArgs g) {
         wait_vmem_lds<0>();
       }
       block_barrier();
-      read(fa[u ^ 1], fb[u ^ 1], st + 1);
       const int buf = (m + (own ? 0 : 1)) & 1;
       const int r0 = rows_lds[buf][w][lane & 15], r1 = rows_lds[buf][w][16 + (lane & 15)];
-      mma(fa[u], fb[u]);
-      // The next stage's 12 LDS reads interleaved with this stage's 32 products (one read
-      // after every two products), so the reads and the address arithmetic fill the
-      // matrix pipe's busy cycles instead of running between the product blocks.
+      const int slot1 = (st + 1) & (kTileStages - 1);
+      // Stage gs + 1's 12 operand reads interleaved with stage gs's 32 products (about one
+      // read per two products, so the reads and the address arithmetic fill the matrix
+      // pipe's busy cycles), and the requests of stage gs + 4 placed between the products:
+      // the activation runs after 8 of them, the weight runs after 16. Requested after all
+      // 32 (when every wavefront of the compute unit sends its four loads at once) the
+      // steps ran 1-3 % slower.
 #pragma unroll
-      for (int i = 0; i < 14; ++i) {
+      for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) fb[u ^ 1][pp][t] = lds[slot1][1][((2 * wn + pp) * 2 + t) * kRunUnits + lane];
+      mma_rows(fa[u], fb[u], 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // the two row-index reads
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // two MFMA
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      sched_fence();
+      if (request) issue_a(r0, r1, own ? st + 4 : st + 4 - nst);
+      sched_fence();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) fa[u ^ 1][i] = lds[slot1][0][(8 * wm + i) * kRunUnits + lane];
+      mma_rows(fa[u], fb[u], 2);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
       sched_fence();
       if (request) {
-        if (own) issue(cur, r0, r1, st + 4);
-        else issue(nxt, r0, r1, st + 4 - nst);
+        if (own) issue_b(cur, st + 4);
+        else issue_b(nxt, st + 4 - nst);
       }
+      sched_fence();
+#pragma unroll
+      for (int i = 4; i < 8; ++i) fa[u ^ 1][i] = lds[slot1][0][(8 * wm + i) * kRunUnits + lane];
+      mma_rows(fa[u], fb[u], 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      sched_fence();
+      mma_rows(fa[u], fb[u], 6);
+      sched_fence();
       if (st == 0 && m + 1 < n_my) set_rows(nxt, (m + 1) & 1);
       if (++st == nst) {  // workgroup-uniform: tile m done
         epilogue(cur);
