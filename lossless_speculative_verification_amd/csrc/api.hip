@@ -108,14 +108,17 @@ int check_config(const moe_verify_config* c) {
                 c->wdtype == MOE_BF16 ? 4096 : 2048, c->inter);
   if (max_work_items(*c, c->max_positions) > 65535 || (int64_t)c->max_positions * c->top_k > (1ll << 30))
     return fail(MOE_EUNSUPPORTED, "max_positions %d too large", c->max_positions);
-  // The tiled expert GEMM forms each lane's activation offset in 32 bits: its operand
-  // buffers (the normalised rows a [P][H] and the SwiGLU rows h [P*(k+S)+1][I]) must stay
-  // below 4 GiB whenever a pass can take that path.
-  if (c->wdtype == MOE_BF16 && c->hidden >= 256 && c->inter >= 256 && c->max_positions >= MV_TILED_MIN_POSITIONS) {
+  // The tiled GEMM forms each lane's activation offset in 32 bits: its operand buffers
+  // (the normalised rows a [P][H], read by the tiled expert GEMM and the tiled LM head, and
+  // the SwiGLU rows h [P*(k+S)+1][I]) must stay below 4 GiB whenever a pass can take that
+  // path.
+  if (c->wdtype == MOE_BF16 && c->hidden >= 256 && c->max_positions >= MV_TILED_MIN_POSITIONS) {
     const int64_t P = c->max_positions, KS = c->top_k + c->n_shared;
-    const int64_t a_bytes = P * c->hidden * 2, h_bytes = (P * KS + 1) * c->inter * 2;
+    const bool expert_tiles = c->inter >= 256, lm_tiles = c->vocab > 0 && c->max_positions >= mv::kTileM;
+    const int64_t a_bytes = (expert_tiles || lm_tiles) ? P * c->hidden * 2 : 0;
+    const int64_t h_bytes = expert_tiles ? (P * KS + 1) * c->inter * 2 : 0;
     if (a_bytes >= (1ll << 32) || h_bytes >= (1ll << 32))
-      return fail(MOE_EUNSUPPORTED, "max_positions %d: the expert GEMM operands (%lld and %lld bytes) must stay below 4 GiB",
+      return fail(MOE_EUNSUPPORTED, "max_positions %d: the tiled GEMM operands (%lld and %lld bytes) must stay below 4 GiB",
                   c->max_positions, (long long)a_bytes, (long long)h_bytes);
   }
   return MOE_OK;

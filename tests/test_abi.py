@@ -98,6 +98,20 @@ def test_expert_gemm_operands_below_4gib(lib):
     assert lib.moe_verify_check_config(ctypes.byref(_cfg(**f32, max_positions=140000))) == bnd.MOE_OK
 
 
+def test_lm_head_operand_below_4gib(lib):
+    """The tiled LM head reads the normalised rows with the same 32-bit offsets, also when
+    the expert GEMMs stay on the streaming kernel (inter below 256): P*hidden*2 bytes must
+    stay below 2^32 whenever the config has an LM head."""
+    kw = dict(hidden=4096, n_routed=64, top_k=1, n_shared=0, inter=128, n_layers=1, vocab=1000,
+              wdtype=bnd.MOE_BF16)
+    # P * 4096 * 2 < 2^32  <=>  P <= 524287
+    assert lib.moe_verify_check_config(ctypes.byref(_cfg(**kw, max_positions=524287))) == bnd.MOE_OK
+    assert lib.moe_verify_check_config(ctypes.byref(_cfg(**kw, max_positions=524288))) == bnd.MOE_EUNSUPPORTED
+    assert "4 GiB" in bnd.last_error()
+    # without an LM head nothing tiles on these rows
+    assert lib.moe_verify_check_config(ctypes.byref(_cfg(**dict(kw, vocab=0), max_positions=524288))) == bnd.MOE_OK
+
+
 def test_null_config_rejected(lib):
     assert lib.moe_verify_check_config(None) == bnd.MOE_EINVAL
 
