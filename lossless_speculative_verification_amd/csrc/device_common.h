@@ -126,23 +126,45 @@ struct Top2 {
 };
 
 // Merge two records: the larger value wins, the lower index on equal values; the
-// loser's best competes for second place. Commutative and associative.
+// loser's best competes for second place. Commutative and associative. Written with
+// selects only (no branch), so merges of independent records overlap.
 __device__ __forceinline__ Top2 top2_merge(Top2 a, Top2 b) {
-  const bool b_wins = (b.v1 > a.v1) || (b.v1 == a.v1 && b.i1 < a.i1);
-  Top2 r;
-  if (b_wins) {
-    r.v1 = b.v1; r.i1 = b.i1; r.v2 = fmaxf(b.v2, a.v1);
-  } else {
-    r.v1 = a.v1; r.i1 = a.i1; r.v2 = fmaxf(a.v2, b.v1);
+  // (bitwise operators: a short-circuit form compiles to a branch)
+  const bool b_wins = (b.v1 > a.v1) | ((b.v1 == a.v1) & (b.i1 < a.i1));
+  const float w2 = b_wins ? b.v2 : a.v2, l1 = b_wins ? a.v1 : b.v1;
+  return Top2{b_wins ? b.v1 : a.v1, b_wins ? b.i1 : a.i1, fmaxf(w2, l1)};
+}
+
+// Fold value v of column c into a running record whose columns all precede c: v takes
+// first place only when strictly larger (so the lowest index wins on equal values), else
+// competes for second place. A NaN value changes nothing.
+__device__ __forceinline__ void top2_push(Top2& b, float v, int c) {
+  const bool gt = v > b.v1, g2 = v > b.v2;
+  b.v2 = gt ? b.v1 : (g2 ? v : b.v2);
+  b.i1 = gt ? c : b.i1;
+  b.v1 = gt ? v : b.v1;
+}
+
+// The value of lane l ^ mask. Masks 16 and 32 use the gfx950 row swaps (no LDS round trip):
+// swapping a register with itself leaves, in each lane, either its own value or its
+// partner's in one of the two results.
+__device__ __forceinline__ uint32_t lane_xor_u32(uint32_t x, int mask) {
+  if (mask == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return (threadIdx.x & 16) ? r[0] : r[1];
   }
-  return r;
+  if (mask == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return (threadIdx.x & 32) ? r[0] : r[1];
+  }
+  return (uint32_t)__shfl_xor((int)x, mask, kWave);
 }
 
 __device__ __forceinline__ Top2 top2_shfl_xor(Top2 t, int mask) {
   Top2 o;
-  o.v1 = __shfl_xor(t.v1, mask, kWave);
-  o.i1 = __shfl_xor(t.i1, mask, kWave);
-  o.v2 = __shfl_xor(t.v2, mask, kWave);
+  o.v1 = __builtin_bit_cast(float, lane_xor_u32(__builtin_bit_cast(uint32_t, t.v1), mask));
+  o.i1 = (int)lane_xor_u32((uint32_t)t.i1, mask);
+  o.v2 = __builtin_bit_cast(float, lane_xor_u32(__builtin_bit_cast(uint32_t, t.v2), mask));
   return o;
 }
 

@@ -987,6 +987,7 @@ __device__ __forceinline__ void lm_stream(const GemmArgs& g, int row0, int M, in
   };
   auto fold = [&](int q) __attribute__((always_inline)) {  // fold the finished pair q into the running records
     const int cb = 2 * q * 16 + 4 * (lane >> 4);
+    const bool full = (2 * q + 2) * 16 <= g.n_valid;  // every column of the pair is a word
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) {
       Top2 b = best[mt];
@@ -995,11 +996,7 @@ __device__ __forceinline__ void lm_stream(const GemmArgs& g, int row0, int M, in
 #pragma unroll
         for (int i = 0; i < 4; ++i) {  // columns in increasing order: a later equal value never wins
           const int c = cb + 16 * t + i;
-          const float v = (q < g.NQ && c < g.n_valid) ? acc[mt][t][i] : NEG;
-          const bool gt = v > b.v1;
-          b.v2 = gt ? b.v1 : fmaxf(b.v2, v);
-          b.i1 = gt ? c : b.i1;
-          b.v1 = gt ? v : b.v1;
+          top2_push(b, (full | ((q < g.NQ) & (c < g.n_valid))) ? acc[mt][t][i] : NEG, c);
         }
       best[mt] = b;
     }

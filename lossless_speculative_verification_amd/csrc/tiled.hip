@@ -13,6 +13,8 @@
 //         A W_lm^T (float32 logits, never stored), merged later by k_argmax_reduce.
 // With a split plan (cold experts in a second work list of 32-row items) the kernel also
 // runs those items with the streaming unit, on compute units without tiles first.
+#include <type_traits>
+
 #include "launch.h"
 #include "stream_gemm.h"
 
@@ -230,28 +232,44 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_moe_tiled(GemmArgs g) {
       // 32 w + l's record of this column tile. Every lane stores exactly once: lanes with
       // no row of the item write the record slot past the last one.
       const float NEG = -__builtin_huge_valf();
+      // columns past the vocabulary (only in the last column tile) never enter a record
+      // A lane's 16 values of a row: the largest and second largest of the multiset by
+      // running max / median-of-three (order-free), then the lowest column holding the
+      // largest, by a scan from the highest column down. The same record as folding the
+      // values one by one in column order (top2_push), in about half the instructions.
+      auto fold = [&](auto checked) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        Top2 b{NEG, INT_MAX, NEG};
+        for (int i = 0; i < 8; ++i) {
+          float v[16];
+          bool ok[16];
 #pragma unroll
-        for (int pp = 0; pp < 2; ++pp) {
-          const int q = t.nt * kTilePairs + 2 * wn + pp;
+          for (int u = 0; u < 16; ++u) {  // u = 8 pp + 4 tt + j: increasing columns
+            const int pp = u >> 3, tt = (u >> 2) & 1, j = u & 3;
+            const int q = t.nt * kTilePairs + 2 * wn + pp, c = (2 * q + tt) * 16 + 4 * gq + j;
+            ok[u] = !decltype(checked)::value || ((q < g.NQ) & (c < g.n_valid));
+            v[u] = ok[u] ? acc[i][pp][tt][j] : NEG;
+          }
+          float v1 = NEG, v2 = NEG;
 #pragma unroll
-          for (int tt = 0; tt < 2; ++tt)
+          for (int u = 0; u < 16; ++u) {
+            v2 = __builtin_amdgcn_fmed3f(v1, v2, v[u]);
+            v1 = __builtin_amdgcn_fmed3f(v1, v[u], __builtin_huge_valf());
+          }
+          int i1 = INT_MAX;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const int c = (2 * q + tt) * 16 + 4 * gq + j;
-              const float v = (q < g.NQ && c < g.n_valid) ? acc[i][pp][tt][j] : NEG;
-              const bool gt = v > b.v1;
-              b.v2 = gt ? b.v1 : fmaxf(b.v2, v);
-              b.i1 = gt ? c : b.i1;
-              b.v1 = gt ? v : b.v1;
-            }
+          for (int u = 15; u >= 0; --u) {
+            const int pp = u >> 3, tt = (u >> 2) & 1, j = u & 3;
+            const int c = (2 * (t.nt * kTilePairs + 2 * wn + pp) + tt) * 16 + 4 * gq + j;
+            i1 = (ok[u] & (v[u] == v1)) ? c : i1;
+          }
+          Top2 b{v1, v1 > NEG ? i1 : INT_MAX, v2};  // no value above -inf: no column, as one by one
+          b = top2_merge(b, top2_shfl_xor(b, 16));
+          b = top2_merge(b, top2_shfl_xor(b, 32));
+          if (lane < 16) lm_red[wn][128 * wm + 16 * i + lane] = b;
         }
-        b = top2_merge(b, top2_shfl_xor(b, 16));
-        b = top2_merge(b, top2_shfl_xor(b, 32));
-        if (lane < 16) lm_red[wn][128 * wm + 16 * i + lane] = b;
-      }
+      };
+      if ((t.nt + 1) * kTilePairs * 32 <= g.n_valid) fold(std::false_type{});  // workgroup-uniform
+      else fold(std::true_type{});
       wait_vmem_lds<63>();  // this wavefront's LDS writes done (loads in flight stay)
       block_barrier();
       const int r = 32 * w + (lane & 31);
