@@ -71,15 +71,16 @@ int64_t max_split_items(const moe_verify_config& c) {
 bool use_tiled(const moe_verify_config& c, int Tn) {
   return c.wdtype == MOE_BF16 && Tn >= MV_TILED_MIN_POSITIONS && c.hidden >= 256 && c.inter >= 256;
 }
-// The LM head runs on the tiled GEMM (k_moe_tiled<EPI_LM>, 256-row items) from 256 rows on
-// unless the last item would be at most half full: beyond two 128-row blocks the streaming
-// LM head is bound by LDS reads rather than by the weight stream, while a tiled round costs
-// the same for a half-empty item. Measured (one MI355X, full vocabulary): 256 rows 109 vs
-// 122 us streaming, 384: 181 vs 169, 448: 184 vs 226, 512: 185 vs 222, 640: 266 vs 266,
-// 768: 266 vs 307.
+// The LM head runs on the tiled GEMM (k_moe_tiled<EPI_LM>, 256-row items) from 256 rows on,
+// except between 257 and 384 rows (a second item at most half full): beyond two 128-row
+// blocks the streaming LM head is bound by LDS reads rather than by the weight stream, while
+// a tiled round costs the same for a half-empty item. Measured (one MI355X, full vocabulary,
+// tiled vs streaming): 256 rows 99 vs 117 us, 384: 168 vs 164, 448: 167 vs 220, 512: 169 vs
+// 215, 640: 238 vs 256, 768: 242 vs 299.
 bool use_tiled_lm(const moe_verify_config& c, int Tv) {
   const int r = Tv % mv::kTileM;
-  return c.wdtype == MOE_BF16 && c.vocab > 0 && c.hidden >= 256 && Tv >= mv::kTileM && (r == 0 || 2 * r > mv::kTileM);
+  const bool half_empty_second = Tv < 2 * mv::kTileM && r > 0 && 2 * r <= mv::kTileM;
+  return c.wdtype == MOE_BF16 && c.vocab > 0 && c.hidden >= 256 && Tv >= mv::kTileM && !half_empty_second;
 }
 
 int check_config(const moe_verify_config* c) {

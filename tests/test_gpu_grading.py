@@ -320,11 +320,12 @@ def test_split_plan_with_every_workgroup_tiled():
     assert err <= TOL["bf16"] and dec.sum() >= 0.8 * wl.positions
 
 
-@pytest.mark.parametrize("T", [256, 512, 700])
+@pytest.mark.parametrize("T", [256, 384, 512, 640, 700])
 def test_tiled_lm_head_small_model(T):
     """The tiled LM head with the shortest contraction it takes (hidden 256: eight steps per
     tile) and a vocabulary of 1,000 (four column tiles, the last one partial), against the
-    oracle's full-logit argmax; 700 rows: a second item three quarters full."""
+    oracle's full-logit argmax; 700 rows: a third item three quarters full; 640 rows: a half
+    full one (tiled); 384 rows: a half-full second item (the streaming head runs)."""
     wl = WL["layer1_bf16"].with_(name=f"lm_small_t{T}", hidden=256, inter=256, n_routed=8, top_k=2, n_shared=1,
                                  vocab=1000, n_layers=1, batch=T, drafts=0)
     w = W.make_weights(wl)
