@@ -72,9 +72,10 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
  *   0 <= n_shared <= 8, n_layers >= 1, vocab >= 0,
  *   hidden and inter multiples of 128 (bf16) or 64 (f32), and hidden a multiple of 256
  *   (bf16) or 128 (f32) when vocab > 0; hidden <= 4096 (bf16) or 2048 (f32),
- *   inter <= 16384, max_positions >= 1; and when bf16 weights can take the tiled expert
- *   GEMM (hidden and inter >= 256, max_positions >= 256), its operands must stay below
- *   4 GiB: max_positions*hidden*2 and (max_positions*(top_k+n_shared)+1)*inter*2 bytes. */
+ *   inter <= 16384, max_positions >= 1; and when bf16 weights can take the tiled GEMM
+ *   (hidden >= 256 and max_positions >= 256, with inter >= 256 for the expert products or
+ *   vocab > 0 for the LM head), its operands must stay below 4 GiB: max_positions*hidden*2
+ *   bytes, and for the expert products (max_positions*(top_k+n_shared)+1)*inter*2 bytes. */
 typedef struct {
   int32_t hidden;        /* H                                                        */
   int32_t n_routed;      /* E routed experts                                         */
