@@ -111,6 +111,23 @@ def test_tiny_fp32_debug_layer():
     assert err <= TOL["f32"]
 
 
+@pytest.mark.parametrize("B,K", [(16, 3), (1100, 3)])
+def test_wider_fp32_model(B, K):
+    """Float32 weights at a wider shape than the tiny model (hidden 512: eight 256-byte
+    blocks per row, 16 routed experts top-4 + 1 shared, two stacked blocks, vocabulary
+    2,000): 64 positions (the split norm/router kernel, the self-planning gate/up) and
+    4,400 positions (the 16-position norm/router kernel and the chunked plan), against the
+    oracle at the float32 tolerance."""
+    wl = WL["tiny_fp32"].with_(name="fp32_wide", hidden=512, inter=256, n_routed=16, top_k=4, n_shared=1,
+                               n_layers=2, vocab=2000, batch=B, drafts=K, seed=1010)
+    log(f"[fp32 wide] B={B} K={K} T={wl.positions}")
+    x = W.make_hidden(wl)
+    ref = oracle_step(wl)
+    ids, margin, hout = run_step(wl, x, B, K)
+    dec = _check_step(wl, ref, ids, margin, hout, x, min_decisive=int(0.5 * wl.positions))
+    _check_accept(wl, ref["ids"], ids, dec)
+
+
 def test_layer1_bf16_step():
     wl = WL["layer1_bf16"]
     x = W.make_hidden(wl)
