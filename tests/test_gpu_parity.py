@@ -192,6 +192,42 @@ def test_small_bf16_both_gemm_paths(T):
     _check_step(wl, full, None, None, hout, x, min_decisive=T // 4)
 
 
+@pytest.mark.parametrize("wdtype,E,k,S,T", [("f32", 8, 1, 0, 200), ("f32", 8, 8, 1, 200), ("bf16", 64, 1, 2, 300),
+                                             ("bf16", 64, 64, 0, 260), ("bf16", 16, 16, 1, 1100)])
+def test_routing_extremes(wdtype, E, k, S, T):
+    """Top-1 routing (every gate exactly 1), every expert selected (k = E: a dense softmax
+    mixture; at 260 and 1,100 positions on the tiled GEMM with every expert hot), and no
+    shared expert, through one block, against the oracle."""
+    base = WL["tiny_fp32"] if wdtype == "f32" else SMALL_BF16
+    wl = base.with_(name=f"route_{wdtype}_{E}_{k}_{S}", n_routed=E, top_k=k, n_shared=S, n_layers=1, vocab=0,
+                    batch=T, drafts=0, seed=1020 + E + k + S)
+    log(f"[routing extremes] {wdtype} E={E} k={k} S={S} T={T}")
+    from gpu_cases import host_weights
+    x = W.make_hidden(wl)
+    ref = O.moe_layer(wl, host_weights(wl), 0, x)
+    m, tid, tw = run_debug_layer(wl, 0, x)
+    dec = ref["gap"] > GATE  # +inf when k = E: nothing is left out
+    assert dec.sum() > T // 2
+    gtol = 1e-5 if wdtype == "f32" else 1e-3
+    if k == E:
+        # every expert once per position; the slot order (decreasing logit) is not compared,
+        # since 64 logits per position hold near-equal neighbours: gates by expert instead
+        np.testing.assert_array_equal(np.sort(tid, axis=1), np.broadcast_to(np.arange(E), (T, E)))
+        g_gpu, g_ref = np.zeros((T, E)), np.zeros((T, E))
+        np.put_along_axis(g_gpu, tid.astype(np.int64), tw, axis=1)
+        np.put_along_axis(g_ref, np.asarray(ref["ids"], np.int64), ref["gates"], axis=1)
+        assert np.abs(g_gpu - g_ref).max() < gtol
+    else:
+        np.testing.assert_array_equal(tid[dec], ref["ids"][dec])
+        assert np.abs(tw[dec] - ref["gates"][dec]).max() < gtol
+    np.testing.assert_allclose(tw.sum(axis=1), 1.0, atol=1e-5)
+    if k == 1:
+        np.testing.assert_array_equal(tw, 1.0)
+    err = row_rel_err(m[dec], ref["m"][dec])
+    log(f"  decisive {dec.sum()}/{T} m rel err {err:.2e}")
+    assert err <= TOL[wdtype]
+
+
 # 300 positions: streaming LM head; 256 and 448: the tiled LM head (items of 256 rows, the
 # second 3/4 full), with the split plan's cold experts (fewer than 64 rows) among 16
 @pytest.mark.parametrize("B,K", [(75, 3), (300, 0), (64, 3), (112, 3)])
