@@ -744,12 +744,19 @@ __global__ __launch_bounds__(256) void k_plan_scatter(PlanArgs pa) {
   const int beg = min(N, (int)blockIdx.x * kPlanChunk), end = min(N, beg + kPlanChunk);
   seg_hist<NW>(pa, beg, end, hist);
   if (threadIdx.x < kWave) {
-    const int e = threadIdx.x;
+    const int e = threadIdx.x, G = (int)gridDim.x;
     int tot = 0, pre = 0;
-    for (int c = 0; c < (int)gridDim.x; ++c) {
-      const int v = pa.chunk_cnt[c * 64 + e];
-      tot += v;
-      pre += c < (int)blockIdx.x ? v : 0;
+    // the chunks' counts kPlanBatch at a time, all their loads in flight together
+    for (int c0 = 0; c0 < G; c0 += kPlanBatch) {
+      int v[kPlanBatch];
+#pragma unroll
+      for (int u = 0; u < kPlanBatch; ++u) v[u] = pa.chunk_cnt[min(c0 + u, G - 1) * 64 + e];
+#pragma unroll
+      for (int u = 0; u < kPlanBatch; ++u) {
+        const int c = c0 + u;
+        tot += c < G ? v[u] : 0;
+        pre += c < (int)blockIdx.x ? v[u] : 0;
+      }
     }
     if (e >= pa.E) tot = 0;
     expert_offsets(pa, tot, off, wstart, blockIdx.x == 0);
