@@ -17,7 +17,9 @@
 //                k_moe_gemm<DOWN> / k_moe_tiled<DOWN>
 //                              (down projection, one bf16 (or fp32) ybuf row per slot)
 //   then         k_norm_route_split (final combine + residual + RMSNorm, no router)
-//                k_lm_head     (LM-head logits tile by tile, top-1/top-2 per tile, never stored)
+//                k_lm_head / k_moe_tiled<LM>
+//                              (LM-head logits tile by tile, top-1/top-2 per tile, never stored;
+//                               the tiled form from 256 rows)
 //                k_argmax_reduce
 //   and          k_accept
 #include <climits>
