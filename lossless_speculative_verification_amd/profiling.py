@@ -12,9 +12,9 @@
         per-kernel MFMA-busy percentage and bf16 MFMA flop rate from one --pmc run with
         MfmaUtil and SQ_INSTS_VALU_MFMA_MOPS_BF16 plus --kernel-trace (csv output).
 
-The traffic file records the sha256 of the kernel sources; bench.py reports a kernel's
-traffic only while that hash still matches the sources (counters of an older build
-would describe other kernels).
+The traffic file records the sha256 of the kernel sources' code (comments aside); bench.py
+reports a kernel's traffic only while that hash still matches the sources (counters of an
+older build would describe other kernels).
 """
 from __future__ import annotations
 
@@ -34,13 +34,25 @@ CSRC = os.path.join(PKG, "csrc")
 TRAFFIC_RE = re.compile(r"^traffic_bytes_per_launch\s+(\S+)\s+(\d+)\s+fetch\s+(\d+)\s+write\s+(\d+)\s+sha256\s+(\w+)")
 
 
+_TOKEN_RE = re.compile(r'("(?:\\.|[^"\\\n])*"|\'(?:\\.|[^\'\\\n])*\')|//[^\n]*|/\*.*?\*/', re.S)
+
+
+def code_text(src: str) -> str:
+    """The source with its comments removed, horizontal whitespace collapsed and blank lines
+    dropped: what the compiler sees, so that an edit of comments alone keeps the hash."""
+    s = _TOKEN_RE.sub(lambda m: m.group(1) if m.group(1) else " ", src)
+    lines = (" ".join(line.split()) for line in s.splitlines())
+    return "\n".join(line for line in lines if line)
+
+
 def source_sha() -> str:
-    """sha256 over the HIP sources and headers the library is built from."""
+    """sha256 over the code (comments aside) of the HIP sources and headers the library is
+    built from."""
     h = hashlib.sha256()
     for p in sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.h"))):
-        with open(p, "rb") as f:
+        with open(p, encoding="utf-8") as f:
             h.update(os.path.basename(p).encode())
-            h.update(f.read())
+            h.update(code_text(f.read()).encode())
     return h.hexdigest()
 
 

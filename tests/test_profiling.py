@@ -107,3 +107,15 @@ def test_committed_traffic_records_parse():
         assert recs, p
         for m in recs:
             assert int(m.group(2)) == int(m.group(3)) + int(m.group(4))
+
+
+def test_source_hash_ignores_comments_only():
+    # comments and layout leave the hashed code unchanged; a code change does not
+    a = "int f(int x) {  // doubles\n  return 2 * x; /* no overflow check */\n}\n"
+    b = "/* header */\nint f(int x) {\n\n    return 2 * x;\n}   // end\n"
+    c = "int f(int x) {\n  return 3 * x;\n}\n"
+    assert P.code_text(a) == P.code_text(b)
+    assert P.code_text(a) != P.code_text(c)
+    # comment markers inside string and character literals are code
+    s = 'asm volatile("s_nop 0 // x" ::); char q = \'/\';\n'
+    assert P.code_text(s) == s.strip()
