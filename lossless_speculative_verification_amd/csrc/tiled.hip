@@ -103,7 +103,16 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_moe_tiled(GemmArgs g) {
   const int NT = (g.NQ + kTilePairs - 1) / kTilePairs;
   // LM: no work list, the items are the consecutive 256-row blocks of the Tn rows
   const int n_items = EPI == EPI_LM ? (g.Tn + kTileM - 1) / kTileM : *g.n_work;
-  const int n_tiles = n_items * NT;
+  // Down GEMM whose tiles, twice over, and streaming items still fit one round of the
+  // device (small skewed passes): every item is run as two 128-row halves, so twice the
+  // compute units share it; in a half tile the wavefronts of rows 128..255 hold only
+  // padding and skip their products. Such a launch gives every workgroup at most one tile.
+  bool half = false;
+  if constexpr (EPI == EPI_DOWN) {
+    const int units = g.n_work2 ? *g.n_work2 * g.NQ : 0;
+    half = 2 * n_items * NT + (units + 7) / 8 <= (int)gridDim.x;
+  }
+  const int n_tiles = n_items * NT * (half ? 2 : 1);
   // This workgroup's tiles: XCD x (hardware workgroups are dealt to the 8 XCDs in turn)
   // owns the x-th contiguous range of logical tiles, and its nbx workgroups take every
   // nbx-th tile of it, so at any time one XCD works on neighbouring tiles (the row
@@ -140,13 +149,18 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_moe_tiled(GemmArgs g) {
       const int nt = __builtin_amdgcn_readfirstlane(lt / n_items), item = lt - nt * n_items;
       return TileInfo{0, item * kTileM, min(kTileM, g.Tn - item * kTileM), item * kTileM, nt};
     } else {
-      const int item = __builtin_amdgcn_readfirstlane(lt / NT);
+      // half: item-major, the two halves' column tiles after each other
+      const int per = half ? 2 * NT : NT;
+      const int item = __builtin_amdgcn_readfirstlane(lt / per);
+      const int nt = lt - item * per, hf = nt >= NT ? 1 : 0;
       // the work list is not written while the kernel runs: read it as constant memory
       // (a scalar load, which the waits for the direct loads do not count)
       typedef int i32x4_t __attribute__((ext_vector_type(4)));
       typedef const __attribute__((address_space(4))) i32x4_t* const_work_ptr;
       const i32x4_t it = ((const_work_ptr)(uintptr_t)g.work)[item];
-      return TileInfo{it[0], it[1], it[2], it[3], lt - item * NT};
+      if (!half) return TileInfo{it[0], it[1], it[2], it[3], nt};
+      const int h0 = (kTileM / 2) * hf;  // a second half of no rows has M <= 0
+      return TileInfo{it[0], it[1] + h0, min(kTileM / 2, it[2] - h0), it[3] + h0, nt - hf * NT};
     }
   };
   // The A source rows of tile t into rows_lds[buf][w]: lane l < 32 holds the row of row
@@ -330,6 +344,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_moe_tiled(GemmArgs g) {
   // the wait for stage 1 that the first step expects (its count assumes whole stages
   // issued in order, which the prologue's split order is not)
   TileInfo cur = info(0), nxt = cur;
+  if (half && cur.M <= 0) break;  // the empty second half of a short item (its only tile)
   if (n_my > 1) nxt = info(1);
   set_rows(cur, 0);
   issue_b(cur, 0);
@@ -379,6 +394,8 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_moe_tiled(GemmArgs g) {
       const int buf = (m + (own ? 0 : 1)) & 1;
       const int r0 = rows_lds[buf][w][lane & 15], r1 = rows_lds[buf][w][16 + (lane & 15)];
       const int slot1 = (st + 1) & (kTileStages - 1);
+      // (down: a wavefront whose 128 rows are all padding skips its products; its operand
+      // reads and requests stay, as every wavefront's loads fill the shared stage)
       // Stage gs + 1's 12 operand reads interleaved with stage gs's 32 products (about one
       // read per two products, so the reads and the address arithmetic fill the matrix
       // pipe's busy cycles), and the requests of stage gs + 4 placed between the products:
@@ -389,7 +406,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_moe_tiled(GemmArgs g) {
       for (int pp = 0; pp < 2; ++pp)
 #pragma unroll
         for (int t = 0; t < 2; ++t) fb[u ^ 1][pp][t] = lds[slot1][1][((2 * wn + pp) * 2 + t) * kRunUnits + lane];
-      mma_rows(fa[u], fb[u], 0);
+      if (EPI != EPI_DOWN || 128 * wm < cur.M) mma_rows(fa[u], fb[u], 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // the two row-index reads
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -401,7 +418,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_moe_tiled(GemmArgs g) {
       sched_fence();
 #pragma unroll
       for (int i = 0; i < 4; ++i) fa[u ^ 1][i] = lds[slot1][0][(8 * wm + i) * kRunUnits + lane];
-      mma_rows(fa[u], fb[u], 2);
+      if (EPI != EPI_DOWN || 128 * wm < cur.M) mma_rows(fa[u], fb[u], 2);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
@@ -415,14 +432,14 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_moe_tiled(GemmArgs g) {
       sched_fence();
 #pragma unroll
       for (int i = 4; i < 8; ++i) fa[u ^ 1][i] = lds[slot1][0][(8 * wm + i) * kRunUnits + lane];
-      mma_rows(fa[u], fb[u], 4);
+      if (EPI != EPI_DOWN || 128 * wm < cur.M) mma_rows(fa[u], fb[u], 4);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
       sched_fence();
-      mma_rows(fa[u], fb[u], 6);
+      if (EPI != EPI_DOWN || 128 * wm < cur.M) mma_rows(fa[u], fb[u], 6);
       sched_fence();
       if (st == 0 && m + 1 < n_my) set_rows(nxt, (m + 1) & 1);
       if (++st == nst) {  // workgroup-uniform: tile m done

@@ -299,6 +299,32 @@ def test_skewed_debug_layer_all_rows(name, layer):
 # ----------------------------------------------------------------------------- tiled paths at their edges
 
 
+@pytest.mark.parametrize("T,bias", [(300, 3.0), (512, 3.0)])
+def test_half_height_down_tiles(T, bias):
+    """A small skewed pass whose down GEMM runs every 256-row item as two 128-row halves
+    (the doubled tiles and the streaming items fit one round of compute units): hot experts
+    with a partial second half (300 positions: about 224 rows each) or an empty one (512:
+    a 127-row second item), shared experts' 44-row item; one block on every row."""
+    wl = WL["skewed_b128_k3"].with_(name=f"half_down_t{T}", n_layers=1, vocab=0, batch=T, drafts=0, bias_value=bias)
+    x = W.make_hidden(wl)
+    ref = O.moe_layer(wl, host_weights(wl), 0, x)
+    counts = np.bincount(ref["ids"].ravel(), minlength=wl.n_routed)
+    hot = counts >= 64  # the split plan's tile experts
+    n_items = int(np.ceil(counts[hot] / 256).sum()) + wl.n_shared * -(-T // 256)
+    units = int(np.ceil(counts[~hot] / 32).sum()) * (wl.hidden // 32)
+    nt = -(-(wl.hidden // 32) // 8)
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    log(f"  items {n_items}, down tiles {n_items * nt} x 2 + {units} streaming units; hot rows {sorted(counts[hot])}")
+    assert 2 * n_items * nt + -(-units // 8) <= n_cu  # the half-height mode is taken
+    m, tid, tw = run_debug_layer(wl, 0, x)
+    dec = ref["gap"] > GATE
+    np.testing.assert_array_equal(tid[dec], ref["ids"][dec])
+    assert np.abs(tw[dec] - ref["gates"][dec]).max() < 1e-3
+    err = row_rel_err(m[dec], ref["m"][dec])
+    log(f"  decisive {dec.sum()}/{wl.positions}, m rel err {err:.2e}")
+    assert err <= TOL["bf16"] and dec.sum() >= 0.8 * wl.positions
+
+
 def test_split_plan_with_every_workgroup_tiled():
     """2,048 positions with 8 hot experts (bias +1.6): the tiles (hot and shared experts)
     exceed one round of compute units, so every workgroup runs streaming items of the cold
