@@ -471,7 +471,9 @@ MV_API int moe_verify_init(const moe_verify_config* cfg, const moe_verify_weight
   c->NQ_up = I / 16;
   c->NQ_dn = (H + 31) / 32;
   c->NQ_lm = (g.vocab + 31) / 32;
-  c->n_pg_lm = (c->NQ_lm + mv::kLmWaves - 1) / mv::kLmWaves;
+  // partial records per row: the streaming head's column groups (at least one pair per
+  // wavefront) or the tiled head's column tiles, whichever is more
+  c->n_pg_lm = std::max((c->NQ_lm + mv::kLmWaves - 1) / mv::kLmWaves, mv::tiled_tiles_per_item(c->NQ_lm));
   c->router_units_per_layer = (size_t)(H * es / 16) * 64;
   c->up_units_per_layer = (size_t)(E + S) * c->NQ_up * c->NKB_H * mv::kPairUnits;
   c->down_units_per_layer = (size_t)(E + S) * c->NQ_dn * c->NKB_I * mv::kPairUnits;
