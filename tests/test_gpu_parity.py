@@ -128,6 +128,25 @@ def test_wider_fp32_model(B, K):
     _check_accept(wl, ref["ids"], ids, dec)
 
 
+@pytest.mark.parametrize("wdtype,H,B,K,L", [("bf16", 4096, 16, 3, 2), ("bf16", 4096, 75, 3, 2), ("bf16", 4096, 1100, 3, 1),
+                                             ("f32", 2048, 16, 3, 2), ("f32", 2048, 1100, 3, 1)])
+def test_widest_rows(wdtype, H, B, K, L):
+    """The widest rows the library takes (hidden 4,096 in bf16, 2,048 in float32): the
+    norm/router kernels' widest register layouts (four float4 per lane and quarter in the
+    split kernel, sixteen per lane in the 16-position kernel) and contractions of 32 K
+    blocks in the streaming and tiled GEMMs and the LM head, at 64, 300 and 4,400
+    positions (8 routed experts top-2 + 1 shared, vocabulary 1,000)."""
+    base = WL["layer1_bf16"] if wdtype == "bf16" else WL["tiny_fp32"]
+    wl = base.with_(name=f"wide_{wdtype}_{H}_b{B}", hidden=H, inter=256, n_routed=8, top_k=2, n_shared=1,
+                    n_layers=L, vocab=1000, batch=B, drafts=K, seed=2020)
+    log(f"[widest rows] {wdtype} H={H} B={B} K={K} L={L} T={wl.positions}")
+    x = W.make_hidden(wl)
+    ref = oracle_step(wl)
+    ids, margin, hout = run_step(wl, x, B, K)
+    dec = _check_step(wl, ref, ids, margin, hout, x, min_decisive=int(0.5 * wl.positions))
+    _check_accept(wl, ref["ids"], ids, dec)
+
+
 def test_layer1_bf16_step():
     wl = WL["layer1_bf16"]
     x = W.make_hidden(wl)
