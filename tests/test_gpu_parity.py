@@ -147,6 +147,22 @@ def test_widest_rows(wdtype, H, B, K, L):
     _check_accept(wl, ref["ids"], ids, dec)
 
 
+@pytest.mark.parametrize("wdtype,B,K", [("bf16", 16, 3), ("bf16", 75, 3), ("f32", 16, 3)])
+def test_widest_intermediate(wdtype, B, K):
+    """The widest expert the library takes (intermediate 16,384, hidden 256): down
+    contractions of 128 K blocks (4,096 columns of h per row block in the tiled kernel)
+    and 1,024 gate/up column pairs per expert, streaming (64 positions) and tiled (300)."""
+    base = WL["layer1_bf16"] if wdtype == "bf16" else WL["tiny_fp32"]
+    wl = base.with_(name=f"wide_inter_{wdtype}_b{B}", hidden=256, inter=16384, n_routed=8, top_k=2, n_shared=1,
+                    n_layers=2, vocab=1000, batch=B, drafts=K, seed=3030)
+    log(f"[widest intermediate] {wdtype} I=16384 B={B} K={K} T={wl.positions}")
+    x = W.make_hidden(wl)
+    ref = oracle_step(wl)
+    ids, margin, hout = run_step(wl, x, B, K)
+    dec = _check_step(wl, ref, ids, margin, hout, x, min_decisive=int(0.5 * wl.positions))
+    _check_accept(wl, ref["ids"], ids, dec)
+
+
 def test_layer1_bf16_step():
     wl = WL["layer1_bf16"]
     x = W.make_hidden(wl)
