@@ -228,11 +228,13 @@ def test_small_bf16_both_gemm_paths(T):
 
 
 @pytest.mark.parametrize("wdtype,E,k,S,T", [("f32", 8, 1, 0, 200), ("f32", 8, 8, 1, 200), ("bf16", 64, 1, 2, 300),
-                                             ("bf16", 64, 64, 0, 260), ("bf16", 16, 16, 1, 1100)])
+                                             ("bf16", 64, 64, 0, 260), ("bf16", 16, 16, 1, 1100),
+                                             ("f32", 1, 1, 1, 64), ("bf16", 1, 1, 0, 300)])
 def test_routing_extremes(wdtype, E, k, S, T):
     """Top-1 routing (every gate exactly 1), every expert selected (k = E: a dense softmax
-    mixture; at 260 and 1,100 positions on the tiled GEMM with every expert hot), and no
-    shared expert, through one block, against the oracle."""
+    mixture; at 260 and 1,100 positions on the tiled GEMM with every expert hot), no
+    shared expert, and a single routed expert (every position on it: a dense block), through
+    one block, against the oracle."""
     base = WL["tiny_fp32"] if wdtype == "f32" else SMALL_BF16
     wl = base.with_(name=f"route_{wdtype}_{E}_{k}_{S}", n_routed=E, top_k=k, n_shared=S, n_layers=1, vocab=0,
                     batch=T, drafts=0, seed=1020 + E + k + S)
