@@ -150,8 +150,8 @@ def test_widest_rows(wdtype, H, B, K, L):
 @pytest.mark.parametrize("wdtype,B,K", [("bf16", 16, 3), ("bf16", 75, 3), ("f32", 16, 3)])
 def test_widest_intermediate(wdtype, B, K):
     """The widest expert the library takes (intermediate 16,384, hidden 256): down
-    contractions of 128 K blocks (4,096 columns of h per row block in the tiled kernel)
-    and 1,024 gate/up column pairs per expert, streaming (64 positions) and tiled (300)."""
+    contractions of 128 K blocks (16,384 elements of h per row) and 1,024 gate/up column
+    pairs per expert, streaming (64 positions) and tiled (300)."""
     base = WL["layer1_bf16"] if wdtype == "bf16" else WL["tiny_fp32"]
     wl = base.with_(name=f"wide_inter_{wdtype}_b{B}", hidden=256, inter=16384, n_routed=8, top_k=2, n_shared=1,
                     n_layers=2, vocab=1000, batch=B, drafts=K, seed=3030)
@@ -370,6 +370,19 @@ def test_prefill_sampled():
     assert err <= TOL["bf16"]
     # the step's block output and the debug hook's agree exactly (same kernels, same order)
     np.testing.assert_array_equal(hout, (x + m).astype(np.float32))
+
+
+def test_largest_pass_sampled():
+    """The largest pass the prefill-shaped model takes (261,882 positions, the work-list
+    bound of its configuration): one block on the tiled path with the chunked plan (768
+    chunks), checked on 256 sampled rows including the first and the last."""
+    wl = WL["prefill_32x1156"].with_(name="prefill_max", batch=261882)
+    x = W.make_hidden(wl)
+    rng = np.random.default_rng(7)
+    rows = tuple(sorted({0, wl.positions - 1} | {int(r) for r in rng.choice(wl.positions, 254, replace=False)}))
+    ref = oracle_step(wl, rows)
+    _, _, hout = run_step(wl, x)
+    _check_step(wl, ref, None, None, hout, x, rows=rows, min_decisive=120)
 
 
 def test_step_rejects_oversize():
