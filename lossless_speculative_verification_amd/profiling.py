@@ -68,21 +68,31 @@ def trace_table(db_path: str) -> str:
         "select name, count(*), avg(end-start)/1000.0, min(end-start)/1000.0, max(end-start)/1000.0, "
         "sum(end-start)/1000.0, max(grid_x), max(vgpr_count), max(accum_vgpr_count), max(lds_size) "
         "from kernels group by name order by sum(end-start) desc").fetchall()
-    out = ["| kernel | calls | avg us | min us | max us | total us | grid (threads) | vgpr/agpr | lds B |",
+    out = ["| kernel | calls | avg us | min us | max us | total us | grid (threads) | vgpr/agpr (trace) | lds B |",
            "|---|---|---|---|---|---|---|---|---|"]
     for r in rows:
         out.append(f"| `{short_name(r[0])[:60]}` | {r[1]} | {r[2]:.2f} | {r[3]:.2f} | {r[4]:.2f} | {r[5]:.1f} | "
                    f"{r[6]} | {r[7]}/{r[8]} | {r[9]} |")
+    out += ["", "The register column is the value the trace database records, which for these kernels is half "
+                "the registers the compiler allocates per lane (e.g. 128 for the 252-register gate/up kernel)."]
     return "\n".join(out)
 
 
-def step_breakdown(db_path: str, marker: str = "k_accept") -> str:
-    """Per-kernel medians within whole verify steps (a step ends with the acceptance kernel),
-    one table per pass shape: steps are grouped by their kernel count and the grid of their
-    first kernel (the routing norm's grid follows the number of positions)."""
+def step_breakdown(db_path: str, marker: Optional[str] = None) -> str:
+    """Per-kernel medians within whole steps, one table per pass shape: steps are grouped
+    by their kernel count and the grid of their first kernel (the routing norm's grid
+    follows the number of positions). A step ends with the kernel named by marker: by
+    default the acceptance kernel, or, in passes without one (no LM head), the final norm
+    (the norm kernel without router)."""
     db = sqlite3.connect(db_path)
     rows = db.execute("select name, start, end, grid_x from kernels order by start").fetchall()
-    acc = [i for i, r in enumerate(rows) if short_name(r[0]).startswith(marker)]
+    names = [short_name(r[0]) for r in rows]
+    if marker is None:
+        marker = "k_accept" if any(n.startswith("k_accept") for n in names) else "k_norm_route_split<"
+        final = marker != "k_accept"
+    else:
+        final = False
+    acc = [i for i, n in enumerate(names) if n.startswith(marker) and (not final or ", false," in n)]
     steps = [rows[a + 1:b + 1] for a, b in zip(acc[:-1], acc[1:])]
     if not steps:
         return "(no complete steps in the trace)"
@@ -99,7 +109,7 @@ def step_breakdown(db_path: str, marker: str = "k_accept") -> str:
                 durs[short_name(name)].append((b - a) / 1000.0)
         spans = [(s[-1][2] - s[0][1]) / 1000.0 for s in ss]
         out += [f"{len(ss)} steps of {n} kernels, first kernel grid {grid} threads; step span median "
-                f"{statistics.median(spans):.1f} us (first kernel start to acceptance end)", "",
+                f"{statistics.median(spans):.1f} us (first kernel start to {'final norm' if final else 'acceptance'} end)", "",
                 "| kernel | launches/step | median us | us/step |", "|---|---|---|---|"]
         for k, v in durs.items():
             per = len(v) // len(ss)

@@ -119,3 +119,20 @@ def test_source_hash_ignores_comments_only():
     # comment markers inside string and character literals are code
     s = 'asm volatile("s_nop 0 // x" ::); char q = \'/\';\n'
     assert P.code_text(s) == s.strip()
+
+
+def test_step_breakdown_ends_passes_without_acceptance_at_the_final_norm(tmp_path):
+    # no acceptance kernel (no LM head): a step ends with the norm kernel without router
+    out, t = [], 0
+    for _ in range(5):
+        for name, dur in (("mv::k_norm_route_split<unsigned short, true, 1, 2, 40>(int)", 9000),
+                          ("mv::k_moe_tiled<0>(int)", 50000),
+                          ("mv::k_norm_route_split<unsigned short, false, 1, 2, 40>(int)", 5000)):
+            out.append((name, t, t + dur, 512))
+            t += dur
+    db = str(tmp_path / "t.db")
+    _trace_db(db, out)
+    res = P.step_breakdown(db)
+    assert res.startswith("4 steps of 3 kernels, first kernel grid 512 threads; step span median 64.0 us "
+                          "(first kernel start to final norm end)")
+    assert "| `k_moe_tiled<0>` | 1 | 50.00 | 50.0 |" in res
